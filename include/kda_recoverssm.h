@@ -1,0 +1,224 @@
+/*
+ * kda_recoverssm.h -- C ABI of the MI355X (gfx950) KDA RecoverSSM library.
+ *
+ * The library implements, for Kimi Delta Attention (KDA) layers served with
+ * speculative decoding, the two device operations the vLLM Kimi-K3 pages
+ * describe:
+ *
+ *   kda_conv_update_verify  -- the speculative verify of one KDA layer with
+ *       the depthwise causal short convolution fused in.  Per request and
+ *       head it runs the gated delta rule over the draft positions starting
+ *       from the request's checkpoint state, writes the outputs, the per-
+ *       position correction and [raw key | raw gate] records, and rolls the
+ *       conv state in place.  The checkpoint is only read.
+ *       (kernels page `vllm.models.kimi_k3.nvidia.recoverssm.kernels`,
+ *       class `CuteRecoverSSMVerify`, method `__call__`; ops page
+ *       `vllm/models/kimi_k3/nvidia/ops/recoverssm.py`, functions
+ *       `_kda_gate`, `_kda_recurrent_step`, `_kda_recoverssm_verify_kernel`,
+ *       `kda_recoverssm_verify`.)
+ *
+ *   kda_recoverssm_commit   -- folds each request's first n accepted
+ *       positions, from those records, into its checkpoint state, for every
+ *       layer in one launch.
+ *       (kernels page, function `cute_recoverssm_commit`; ops page,
+ *       `_commit_kda_state_kernel` and `KDARecoverSSMCommitContext`.)
+ *
+ * plus host-only argument checks mirroring the pages' validation
+ * (kernels page `_check_layouts`, `can_use_cute_recoverssm`; ops page
+ * `kda_recoverssm_verify`, `KDARecoverSSMCommitContext.create/commit`).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are described by kda_tensor: a device pointer, a dtype, and up
+ *    to four sizes and strides, strides counted in ELEMENTS.  Every pointer
+ *    handed to the library is a device pointer unless stated otherwise.
+ *  - The caller owns every buffer.  The library allocates no device memory,
+ *    keeps no pointer after a call returns and performs no host/device
+ *    synchronisation.  Launches are asynchronous on the given stream (a
+ *    hipStream_t passed as void*; NULL = the null stream), so both launches
+ *    may be captured in a HIP graph.
+ *  - Every entry point returns KDA_OK (0) or a kda_status code; a failing
+ *    call launches nothing and leaves a message for kda_last_error() in the
+ *    calling thread.  Zero-sized work (batch 0 or no tokens) returns KDA_OK
+ *    without launching.
+ *  - Values that live on the device (query lengths, slots, accepted counts,
+ *    commit lengths, record rows) are never read by the host.  The kernels
+ *    clamp them instead: query length to [0, Q], accepted count to [1, Q],
+ *    commit length to [0, Q]; a slot <= null_block_id or >= the pool size is
+ *    null; a record row outside [0, rows) writes (verify) or reads (commit)
+ *    no records.
+ *  - Two requests of one launch must not name the same non-null slot, and a
+ *    commit's final slot must not be another request's source slot; the
+ *    pages leave these cases undefined and so does this library.
+ */
+#ifndef KDA_RECOVERSSM_H
+#define KDA_RECOVERSSM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+/* Status codes. */
+typedef enum {
+  KDA_OK = 0,
+  KDA_E_SHAPE = 1,       /* sizes disagree with each other */
+  KDA_E_DTYPE = 2,       /* an element type that is not accepted */
+  KDA_E_LAYOUT = 3,      /* strides or alignment of a cache page or
+                            parameter tensor (kernels page `_check_layouts`) */
+  KDA_E_UNALIGNED = 4,   /* a per-step activation does not start on a
+                            16-byte boundary; nothing is launched and the
+                            caller may run another implementation (kernels
+                            page, `CuteRecoverSSMVerify.__call__` returns
+                            False in that case) */
+  KDA_E_UNSUPPORTED = 5, /* head dim not in {16,32,64,128}, conv width not
+                            4, window Q not in 1..16 */
+  KDA_E_CAPACITY = 6,    /* more tokens than batch * Q (ops page,
+                            `kda_recoverssm_verify`) */
+  KDA_E_DEVICE = 7,      /* a HIP runtime error */
+  KDA_E_ARG = 8          /* a required pointer is NULL or a count is
+                            negative */
+} kda_status;
+
+/* Element types. */
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* A strided tensor view.  `stride` is in elements; unused trailing entries
+   of shape/stride are ignored. */
+typedef struct {
+  void* data;
+  int32_t dtype;     /* kda_dtype */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} kda_tensor;
+
+/* Arguments of kda_conv_update_verify.  H = number of heads, D = head dim
+   (= key dim = value dim), T = token rows, Q = spec_query_len (draft window),
+   W = 4 conv taps, Lc = Q + W - 2 conv-state length, N state slots, R record
+   rows.  "act" is the activation dtype (F32 or BF16) shared by mixed_qkv,
+   raw_gate, raw_beta and conv_state. */
+typedef struct {
+  kda_tensor mixed_qkv;    /* act [T, 3HD]: raw q|k|v projections before the
+                              convolution; channel = part*H*D + h*D + d */
+  kda_tensor raw_gate;     /* act [T, HD]: gate input before dt_bias */
+  kda_tensor raw_beta;     /* act [T, H]: beta before the sigmoid */
+  kda_tensor A_log;        /* F32 [H], contiguous */
+  kda_tensor dt_bias;      /* F32 [H, D] (or [H*D]), contiguous */
+  kda_tensor state;        /* F32 [N, H, D(v), D(k)]: checkpoint pool, read
+                              only; strides (any, D*D, D, 1), slot stride a
+                              multiple of 16 bytes */
+  kda_tensor correction;   /* F32 [R, H, Q, D]: correction record */
+  kda_tensor key_gate;     /* F32 or act [R, H, Q, 2D]: [0,D) post-conv raw
+                              key, [D,2D) raw gate */
+  kda_tensor out;          /* F32 or act [T, HD] */
+  kda_tensor conv_state;   /* act; dim-first [N, 3HD, Lc] or token-first
+                              [N, Lc, 3HD] (see conv_dim_first); rolled in
+                              place */
+  kda_tensor conv_weight;  /* F32 or act [3HD, W]; weight[:, W-1] multiplies
+                              the newest input */
+  const int32_t* query_start_loc;      /* [batch+1] token offsets */
+  const int32_t* state_indices;        /* [batch] checkpoint slots */
+  const int32_t* num_accepted_tokens;  /* [batch] conv history offset + 1 */
+  const int32_t* record_rows;          /* [batch] record row, or NULL: the
+                                          request's state slot */
+  int32_t* work_counter;   /* device int32[1]: ticket counter.  Must be 0
+                              before the first launch; every launch leaves it
+                              at 0.  One counter per launch in flight. */
+  int32_t batch;
+  int32_t spec_query_len;  /* Q */
+  int32_t null_block_id;   /* slots <= this are null (0 in vLLM) */
+  int32_t conv_dim_first;  /* 1: conv_state is [N, 3HD, Lc]; 0: [N, Lc, 3HD] */
+  int32_t use_lower_bound; /* 1: g = lower_bound*sigmoid(A x); 0: softplus */
+  float lower_bound;
+  int32_t max_workgroups;  /* persistent grid size; 0 = one full wave of
+                              resident workgroups on the device */
+  int32_t reserved;
+} kda_verify_args;
+
+/* Arguments of kda_recoverssm_commit.  Per-layer tensors are described by
+   device tables of int64 base byte addresses and slot (row) strides in
+   elements, as the ops page's commit context builds them; inner strides
+   are shared by all layers. */
+typedef struct {
+  int32_t num_layers;          /* L >= 1 */
+  int32_t batch;
+  int32_t num_heads;           /* H */
+  int32_t head_dim;            /* D */
+  int32_t spec_query_len;      /* Q */
+  int32_t null_block_id;
+  int64_t num_slots;           /* N of every layer's state pool */
+  int64_t num_record_rows;     /* R of every layer's records */
+  /* device int64[L] tables */
+  const int64_t* state_base_addrs;          /* F32 [N, H, D, D] views */
+  const int64_t* state_block_strides;
+  const int64_t* correction_base_addrs;     /* F32 [R, H, Q, D] views */
+  const int64_t* correction_block_strides;
+  const int64_t* key_gate_base_addrs;       /* [R, H, Q, 2D] views */
+  const int64_t* key_gate_block_strides;
+  int64_t state_strides[2];       /* head, row; must be (D*D, D) */
+  int64_t correction_strides[2];  /* head, position; dim stride is 1 */
+  int64_t key_gate_strides[2];    /* head, position; dim stride is 1 */
+  int32_t key_gate_dtype;         /* kda_dtype */
+  int32_t reserved0;
+  const float* A_log;             /* device F32 [L, H] */
+  int64_t A_log_strides[2];
+  const float* dt_bias;           /* device F32 [L, H, D] */
+  int64_t dt_bias_strides[3];
+  const int32_t* use_lower_bound; /* device int32 [L]: gate kind per layer */
+  const float* lower_bound;       /* device F32 [L] */
+  const int32_t* state_indices;   /* device [batch] source slots */
+  const int32_t* commit_lens;     /* device [batch] accepted positions */
+  const int32_t* final_state_indices; /* device [batch] or NULL: in place */
+  const int32_t* record_rows;     /* device [batch] or NULL: source slot */
+  /* Optional HOST copy of the six device tables, laid out as int64[6][L] in
+     the order above (state bases, state strides, correction bases,
+     correction strides, key/gate bases, key/gate strides).  When given,
+     the checks verify every layer's alignment; NULL skips those checks. */
+  const int64_t* host_tables;
+} kda_commit_args;
+
+/* Library ABI version (KDA_ABI_VERSION). */
+int kda_abi_version(void);
+
+/* Message of the last failing call in this thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Name of a status code. */
+const char* kda_status_string(int status);
+
+/* Host-only validation of verify arguments: shapes, dtypes, strides,
+   alignment and supported sizes.  Reads no device memory, launches nothing.
+   (kernels page `_check_layouts`, `can_use_cute_recoverssm`; ops page
+   `kda_recoverssm_verify`.) */
+int kda_check_verify(const kda_verify_args* args);
+
+/* Validate, then launch the fused conv update + speculative verify on
+   `stream`.  Writes out, correction/key_gate records of the written
+   positions, and the rolled conv state; leaves state and every other byte
+   unchanged; null requests get +0.0 outputs and nothing else. */
+int kda_conv_update_verify(const kda_verify_args* args, void* stream);
+
+/* Host-only validation of commit arguments (ops page
+   `KDARecoverSSMCommitContext.create` and `.commit`). */
+int kda_check_commit(const kda_commit_args* args);
+
+/* Validate, then launch the multi-layer commit on `stream`: for every layer
+   and request with a non-null source slot, a non-null final slot, a valid
+   record row and n = commit length > 0, the checkpoint of every head
+   becomes S_n = S_0 * prod_t diag(exp g_t) + sum_t c_t k_hat_t^T
+   * prod_{s>t} diag(exp g_s) over t < n, stored at the final slot. */
+int kda_recoverssm_commit(const kda_commit_args* args, void* stream);
+
+/* Launch a one-workgroup kernel that sets counter[0..n) to 0 on `stream`
+   (for a counter left non-zero by an aborted launch).  Uses no memset
+   node, so it may be captured in a graph. */
+int kda_reset_counter(int32_t* counter, int32_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_RECOVERSSM_H */

@@ -1,0 +1,17 @@
+"""MI355X-native KDA RecoverSSM speculative verify and commit.
+
+The compute path is the HIP library `libkda_recoverssm.so` (C ABI in
+include/kda_recoverssm.h); this package is its thin torch binding.
+"""
+from ._abi import LIB_PATH, load  # noqa: F401
+from .ops import (  # noqa: F401
+    CommitContext,
+    KdaError,
+    KdaUnaligned,
+    abi_version,
+    check_verify,
+    conv_update_verify,
+    describe,
+    reset_counter,
+    verify_args,
+)

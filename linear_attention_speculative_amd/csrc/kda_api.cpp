@@ -1,0 +1,504 @@
+// Host side of the KDA RecoverSSM library: argument checks (mirroring the
+// validation of the kernels page's `_check_layouts` and
+// `can_use_cute_recoverssm` and the ops page's `kda_recoverssm_verify` and
+// `KDARecoverSSMCommitContext.create/commit`), translation of the public
+// descriptors into launch parameters, and the exported C entry points.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "kda_internal.hpp"
+#include "kda_recoverssm.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int elem_size(int32_t dt) {
+  return dt == KDA_F32 ? 4 : (dt == KDA_BF16 ? 2 : 0);
+}
+
+bool aligned(const void* p, uintptr_t a) {
+  return reinterpret_cast<uintptr_t>(p) % a == 0;
+}
+
+const char* dt_name(int32_t dt) {
+  return dt == KDA_F32 ? "float32" : (dt == KDA_BF16 ? "bfloat16" : "?");
+}
+
+bool supported_head_dim(int64_t d) {
+  return d == 16 || d == 32 || d == 64 || d == 128;
+}
+
+// Checks ndim, non-negative sizes, known dtype and a data pointer.
+int check_desc(const kda_tensor& t, const char* name, int ndim) {
+  if (t.ndim != ndim)
+    return fail(KDA_E_SHAPE, "%s must have %d dimensions (got %d)", name,
+                ndim, t.ndim);
+  for (int i = 0; i < ndim; ++i)
+    if (t.shape[i] < 0)
+      return fail(KDA_E_SHAPE, "%s has a negative size", name);
+  if (elem_size(t.dtype) == 0)
+    return fail(KDA_E_DTYPE, "%s has an unknown dtype code %d", name,
+                t.dtype);
+  int64_t numel = 1;
+  for (int i = 0; i < ndim; ++i) numel *= t.shape[i];
+  if (t.data == nullptr && numel > 0)
+    return fail(KDA_E_ARG, "%s has no data pointer", name);
+  return KDA_OK;
+}
+
+bool shape_is(const kda_tensor& t, int64_t a, int64_t b, int64_t c = -1,
+              int64_t d = -1) {
+  if (t.shape[0] != a || t.shape[1] != b) return false;
+  if (c >= 0 && t.shape[2] != c) return false;
+  if (d >= 0 && t.shape[3] != d) return false;
+  return true;
+}
+
+struct VerifyPlan {
+  kda::VerifyParams p;
+  int D = 0;
+  bool act_bf16 = false;
+  bool noop = false;
+  int grid = 0;
+};
+
+#define KDA_TRY(expr)             \
+  do {                            \
+    int rc_ = (expr);             \
+    if (rc_ != KDA_OK) return rc_; \
+  } while (0)
+
+int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
+  if (a == nullptr) return fail(KDA_E_ARG, "verify arguments are NULL");
+  if (a->batch < 0) return fail(KDA_E_ARG, "batch is negative");
+  const int64_t Q = a->spec_query_len;
+  if (Q < 1 || Q > kda::kMaxWindow)
+    return fail(KDA_E_UNSUPPORTED,
+                "KDA RecoverSSM verify supports 1 to %d draft positions per "
+                "step (got %lld)",
+                kda::kMaxWindow, (long long)Q);
+
+  // Parameters and pool: heads, head dim, slots.
+  KDA_TRY(check_desc(a->A_log, "A_log", 1));
+  KDA_TRY(check_desc(a->state, "state", 4));
+  const kda_tensor& S = a->state;
+  const int64_t H = a->A_log.shape[0];
+  const int64_t N = S.shape[0];
+  const int64_t D = S.shape[3];
+  if (H < 1) return fail(KDA_E_SHAPE, "A_log must hold one value per head");
+  if (S.dtype != KDA_F32)
+    return fail(KDA_E_DTYPE, "the checkpoint state must be float32");
+  if (!supported_head_dim(D))
+    return fail(KDA_E_UNSUPPORTED,
+                "head dim %lld is not supported (16, 32, 64 or 128)",
+                (long long)D);
+  if (S.shape[1] != H || S.shape[2] != D)
+    return fail(KDA_E_SHAPE,
+                "checkpoint shape [%lld, %lld, %lld, %lld] does not match "
+                "[slots, heads=%lld, %lld, %lld]",
+                (long long)S.shape[0], (long long)S.shape[1],
+                (long long)S.shape[2], (long long)S.shape[3], (long long)H,
+                (long long)D, (long long)D);
+  if (N < 1) return fail(KDA_E_SHAPE, "the state pool has no slots");
+  if (S.stride[1] != D * D || S.stride[2] != D || S.stride[3] != 1 ||
+      (S.stride[0] * 4) % 16 != 0)
+    return fail(KDA_E_LAYOUT,
+                "state strides (%lld, %lld, %lld, %lld) need contiguous "
+                "heads and 16-byte aligned slots",
+                (long long)S.stride[0], (long long)S.stride[1],
+                (long long)S.stride[2], (long long)S.stride[3]);
+  if (a->A_log.dtype != KDA_F32 || a->A_log.stride[0] != 1)
+    return fail(a->A_log.dtype != KDA_F32 ? KDA_E_DTYPE : KDA_E_LAYOUT,
+                "A_log must be a contiguous float32 vector");
+  const kda_tensor& dtb = a->dt_bias;
+  if (dtb.ndim != 1 && dtb.ndim != 2)
+    return fail(KDA_E_SHAPE, "dt_bias must be [H*D] or [H, D]");
+  KDA_TRY(check_desc(dtb, "dt_bias", dtb.ndim));
+  if (dtb.dtype != KDA_F32)
+    return fail(KDA_E_DTYPE, "dt_bias must be float32");
+  if (dtb.ndim == 1 ? (dtb.shape[0] != H * D || dtb.stride[0] != 1)
+                    : (dtb.shape[0] != H || dtb.shape[1] != D ||
+                       dtb.stride[1] != 1 || dtb.stride[0] != D))
+    return fail(KDA_E_SHAPE,
+                "dt_bias must hold heads*head_dim contiguous values");
+
+  // Activations.
+  KDA_TRY(check_desc(a->mixed_qkv, "mixed_qkv", 2));
+  KDA_TRY(check_desc(a->raw_gate, "raw_gate", 2));
+  KDA_TRY(check_desc(a->raw_beta, "raw_beta", 2));
+  KDA_TRY(check_desc(a->out, "out", 2));
+  const int32_t act = a->mixed_qkv.dtype;
+  const int64_t T = a->mixed_qkv.shape[0];
+  const int64_t HD = H * D;
+  if (a->raw_gate.dtype != act || a->raw_beta.dtype != act)
+    return fail(KDA_E_DTYPE,
+                "mixed_qkv, raw_gate and raw_beta must share one dtype");
+  if (!shape_is(a->mixed_qkv, T, 3 * HD))
+    return fail(KDA_E_SHAPE, "mixed_qkv must be [T, 3*H*D] = [%lld, %lld]",
+                (long long)T, (long long)(3 * HD));
+  if (!shape_is(a->raw_gate, T, HD) || !shape_is(a->raw_beta, T, H))
+    return fail(KDA_E_SHAPE,
+                "KDA RecoverSSM gate or beta shape is incompatible");
+  if (!shape_is(a->out, T, HD))
+    return fail(KDA_E_SHAPE, "KDA RecoverSSM output shape is incompatible");
+  if (a->out.dtype != KDA_F32 && a->out.dtype != act)
+    return fail(KDA_E_DTYPE, "out must be float32 or the activation dtype");
+  if (a->mixed_qkv.stride[1] != 1 || a->raw_gate.stride[1] != 1 ||
+      a->raw_beta.stride[1] != 1 || a->out.stride[1] != 1)
+    return fail(KDA_E_LAYOUT,
+                "KDA RecoverSSM activation and output heads must be "
+                "contiguous");
+
+  // Records.
+  KDA_TRY(check_desc(a->correction, "correction", 4));
+  KDA_TRY(check_desc(a->key_gate, "key_gate", 4));
+  const int64_t R = a->correction.shape[0];
+  if (!shape_is(a->correction, R, H, Q, D))
+    return fail(KDA_E_SHAPE,
+                "KDA RecoverSSM correction buffer needs shape [rows, %lld, "
+                "%lld, %lld]",
+                (long long)H, (long long)Q, (long long)D);
+  if (!shape_is(a->key_gate, R, H, Q, 2 * D))
+    return fail(KDA_E_SHAPE,
+                "KDA RecoverSSM key/gate buffer needs shape [%lld, %lld, "
+                "%lld, %lld]",
+                (long long)R, (long long)H, (long long)Q, (long long)(2 * D));
+  if (a->correction.dtype != KDA_F32)
+    return fail(KDA_E_DTYPE,
+                "KDA RecoverSSM correction buffer must use float32");
+  if (a->key_gate.dtype != KDA_F32 && a->key_gate.dtype != act)
+    return fail(KDA_E_DTYPE,
+                "the key/gate buffer must be float32 or the activation "
+                "dtype");
+  if (a->correction.stride[3] != 1 || a->key_gate.stride[3] != 1)
+    return fail(KDA_E_LAYOUT, "record rows must be contiguous");
+
+  // Conv state and weight.
+  KDA_TRY(check_desc(a->conv_state, "conv_state", 3));
+  KDA_TRY(check_desc(a->conv_weight, "conv_weight", 2));
+  const kda_tensor& cs = a->conv_state;
+  const int64_t C3 = 3 * HD;
+  const int64_t Lc = a->conv_dim_first ? cs.shape[2] : cs.shape[1];
+  const int64_t cdim = a->conv_dim_first ? cs.shape[1] : cs.shape[2];
+  if (cs.shape[0] != N || cdim != C3)
+    return fail(KDA_E_SHAPE,
+                "conv state must be [slots=%lld, %lld, Lc] (dim first) or "
+                "[slots, Lc, %lld] (token first)",
+                (long long)N, (long long)C3, (long long)C3);
+  if (cs.dtype != act)
+    return fail(KDA_E_DTYPE,
+                "the conv state must use the activation dtype (%s)",
+                dt_name(act));
+  if (Lc - Q + 2 != kda::kConvWidth)
+    return fail(KDA_E_UNSUPPORTED,
+                "conv state length %lld implies a width-%lld convolution; "
+                "only width %d is supported (length = Q + 2)",
+                (long long)Lc, (long long)(Lc - Q + 2), kda::kConvWidth);
+  if (!shape_is(a->conv_weight, C3, kda::kConvWidth))
+    return fail(KDA_E_SHAPE, "conv_weight must be [%lld, %d]",
+                (long long)C3, kda::kConvWidth);
+  if (a->conv_weight.dtype != KDA_F32 && a->conv_weight.dtype != act)
+    return fail(KDA_E_DTYPE,
+                "conv_weight must be float32 or the activation dtype");
+
+  // Capacity (ops page: more tokens than the window allows is an error).
+  if (T > int64_t(a->batch) * Q)
+    return fail(KDA_E_CAPACITY,
+                "KDA RecoverSSM speculative decode input exceeds its "
+                "activation capacity (%lld tokens > %d x %lld)",
+                (long long)T, a->batch, (long long)Q);
+  if (int64_t(a->batch) * H > 0x7fffffff || T > 0x7fffffff)
+    return fail(KDA_E_CAPACITY, "batch * heads or tokens exceed 2^31");
+
+  // Static tensors: 16-byte starts (kernels page `_check_layouts`).
+  const kda_tensor* statics[] = {&a->state, &a->A_log, &a->dt_bias,
+                                 &a->correction, &a->key_gate,
+                                 &a->conv_state, &a->conv_weight};
+  const char* snames[] = {"state", "A_log", "dt_bias", "correction",
+                          "key_gate", "conv_state", "conv_weight"};
+  for (int i = 0; i < 7; ++i)
+    if (!aligned(statics[i]->data, 16))
+      return fail(KDA_E_LAYOUT,
+                  "KDA RecoverSSM: %s must start on a 16-byte boundary",
+                  snames[i]);
+  const int ek = elem_size(a->key_gate.dtype);
+  for (int i = 0; i < 3; ++i)
+    if ((a->correction.stride[i] * 4) % 16 != 0 ||
+        (a->key_gate.stride[i] * ek) % 16 != 0)
+      return fail(KDA_E_LAYOUT,
+                  "record slot, head and position strides must be "
+                  "multiples of 16 bytes");
+
+  // Per-step tensors: not launched when misaligned (the caller may fall
+  // back, as the kernels page's verify returns False).
+  const int ea = elem_size(act), eo = elem_size(a->out.dtype);
+  if (!aligned(a->mixed_qkv.data, 16) || !aligned(a->raw_gate.data, 16) ||
+      !aligned(a->out.data, 16) ||
+      (a->mixed_qkv.stride[0] * ea) % 16 != 0 ||
+      (a->raw_gate.stride[0] * ea) % 16 != 0 ||
+      (a->out.stride[0] * eo) % 16 != 0)
+    return fail(KDA_E_UNALIGNED,
+                "an activation or output row does not start on a 16-byte "
+                "boundary");
+  if (!aligned(a->raw_beta.data, ea))
+    return fail(KDA_E_UNALIGNED, "raw_beta is not element aligned");
+
+  // Metadata.
+  if (a->batch > 0) {
+    if (!a->query_start_loc || !a->state_indices || !a->num_accepted_tokens)
+      return fail(KDA_E_ARG,
+                  "query_start_loc, state_indices and num_accepted_tokens "
+                  "are required");
+    if (!a->work_counter) return fail(KDA_E_ARG, "work_counter is NULL");
+    const void* ptrs[] = {a->query_start_loc, a->state_indices,
+                          a->num_accepted_tokens, a->record_rows,
+                          a->work_counter};
+    for (const void* q : ptrs)
+      if (q && !aligned(q, 4))
+        return fail(KDA_E_UNALIGNED, "metadata pointers must be 4-byte "
+                                     "aligned");
+  }
+
+  kda::VerifyParams& p = plan->p;
+  p = kda::VerifyParams{};
+  p.mixed_qkv = a->mixed_qkv.data;
+  p.s_x = a->mixed_qkv.stride[0];
+  p.raw_gate = a->raw_gate.data;
+  p.s_g = a->raw_gate.stride[0];
+  p.raw_beta = a->raw_beta.data;
+  p.s_beta = a->raw_beta.stride[0];
+  p.A_log = static_cast<const float*>(a->A_log.data);
+  p.dt_bias = static_cast<const float*>(dtb.data);
+  p.state = static_cast<const float*>(S.data);
+  p.s_slot = S.stride[0];
+  p.correction = static_cast<float*>(a->correction.data);
+  p.s_c_row = a->correction.stride[0];
+  p.s_c_head = a->correction.stride[1];
+  p.s_c_pos = a->correction.stride[2];
+  p.key_gate = a->key_gate.data;
+  p.s_kg_row = a->key_gate.stride[0];
+  p.s_kg_head = a->key_gate.stride[1];
+  p.s_kg_pos = a->key_gate.stride[2];
+  p.out = a->out.data;
+  p.s_out = a->out.stride[0];
+  p.conv_state = cs.data;
+  p.s_cs_slot = cs.stride[0];
+  p.s_cs_chan = a->conv_dim_first ? cs.stride[1] : cs.stride[2];
+  p.s_cs_tok = a->conv_dim_first ? cs.stride[2] : cs.stride[1];
+  p.conv_weight = a->conv_weight.data;
+  p.s_w_chan = a->conv_weight.stride[0];
+  p.s_w_tap = a->conv_weight.stride[1];
+  p.qsl = a->query_start_loc;
+  p.slots = a->state_indices;
+  p.accepted = a->num_accepted_tokens;
+  p.record_rows = a->record_rows;
+  p.counter = a->work_counter;
+  p.B = a->batch;
+  p.H = int32_t(H);
+  p.Q = int32_t(Q);
+  p.N = N > 0x7fffffff ? 0x7fffffff : int32_t(N);
+  p.R = R > 0x7fffffff ? 0x7fffffff : int32_t(R);
+  p.T = int32_t(T);
+  p.null_id = a->null_block_id;
+  p.out_bf16 = a->out.dtype == KDA_BF16;
+  p.kg_bf16 = a->key_gate.dtype == KDA_BF16;
+  p.w_bf16 = a->conv_weight.dtype == KDA_BF16;
+  p.use_lb = a->use_lower_bound != 0;
+  p.lb = a->lower_bound;
+  p.n_items = int32_t(int64_t(a->batch) * H);
+  plan->D = int(D);
+  plan->act_bf16 = act == KDA_BF16;
+  plan->noop = a->batch == 0 || T == 0;
+  plan->grid = a->max_workgroups;
+  return KDA_OK;
+}
+
+struct CommitPlan {
+  kda::CommitParams p;
+  int D = 0;
+  bool noop = false;
+};
+
+int plan_commit(const kda_commit_args* a, CommitPlan* plan) {
+  if (a == nullptr) return fail(KDA_E_ARG, "commit arguments are NULL");
+  if (a->num_layers < 1)
+    return fail(KDA_E_ARG, "KDA RecoverSSM commit requires at least one "
+                           "layer");
+  if (a->batch < 0) return fail(KDA_E_ARG, "batch is negative");
+  const int64_t H = a->num_heads, D = a->head_dim, Q = a->spec_query_len;
+  if (H < 1) return fail(KDA_E_SHAPE, "num_heads must be positive");
+  if (!supported_head_dim(D))
+    return fail(KDA_E_UNSUPPORTED,
+                "head dim %lld is not supported (16, 32, 64 or 128)",
+                (long long)D);
+  if (Q < 1 || Q > kda::kMaxWindow)
+    return fail(KDA_E_UNSUPPORTED,
+                "KDA RecoverSSM commit supports windows of 1 to %d",
+                kda::kMaxWindow);
+  if (a->num_slots < 1 || a->num_record_rows < 1)
+    return fail(KDA_E_SHAPE, "the state pool and records need rows");
+  if (!a->state_base_addrs || !a->state_block_strides ||
+      !a->correction_base_addrs || !a->correction_block_strides ||
+      !a->key_gate_base_addrs || !a->key_gate_block_strides)
+    return fail(KDA_E_ARG, "the per-layer address tables are required");
+  if (!a->A_log || !a->dt_bias || !a->use_lower_bound || !a->lower_bound)
+    return fail(KDA_E_ARG, "the stacked gate parameters are required");
+  if (a->batch > 0 && (!a->state_indices || !a->commit_lens))
+    return fail(KDA_E_ARG, "state_indices and commit_lens are required");
+  if (a->state_strides[0] != D * D || a->state_strides[1] != D)
+    return fail(KDA_E_LAYOUT,
+                "KDA RecoverSSM layers need contiguous checkpoint heads "
+                "(strides %lld, %lld)",
+                (long long)a->state_strides[0],
+                (long long)a->state_strides[1]);
+  const int ek = elem_size(a->key_gate_dtype);
+  if (ek == 0) return fail(KDA_E_DTYPE, "key/gate dtype must be F32 or BF16");
+  for (int i = 0; i < 2; ++i)
+    if ((a->correction_strides[i] * 4) % 16 != 0 ||
+        (a->key_gate_strides[i] * ek) % 16 != 0)
+      return fail(KDA_E_LAYOUT,
+                  "record head and position strides must be multiples of "
+                  "16 bytes");
+  if (int64_t(a->num_layers) * a->batch * H > 0x7fffffff)
+    return fail(KDA_E_CAPACITY, "layers * batch * heads exceeds 2^31");
+  if (a->host_tables) {
+    const int64_t L = a->num_layers;
+    const int64_t* t = a->host_tables;
+    const int esz[3] = {4, 4, ek};
+    const char* nm[3] = {"state", "correction", "key/gate"};
+    for (int k = 0; k < 3; ++k)
+      for (int64_t l = 0; l < L; ++l) {
+        const int64_t base = t[(2 * k) * L + l];
+        const int64_t bs = t[(2 * k + 1) * L + l];
+        if (base == 0 || base % 16 != 0 || (bs * esz[k]) % 16 != 0)
+          return fail(KDA_E_LAYOUT,
+                      "layer %lld: %s view must start on a 16-byte boundary "
+                      "with 16-byte aligned slots",
+                      (long long)l, nm[k]);
+      }
+  }
+  kda::CommitParams& p = plan->p;
+  p = kda::CommitParams{};
+  p.state_base = a->state_base_addrs;
+  p.state_bs = a->state_block_strides;
+  p.corr_base = a->correction_base_addrs;
+  p.corr_bs = a->correction_block_strides;
+  p.kg_base = a->key_gate_base_addrs;
+  p.kg_bs = a->key_gate_block_strides;
+  p.s_state_head = a->state_strides[0];
+  p.s_c_head = a->correction_strides[0];
+  p.s_c_pos = a->correction_strides[1];
+  p.s_kg_head = a->key_gate_strides[0];
+  p.s_kg_pos = a->key_gate_strides[1];
+  p.A_log = a->A_log;
+  p.s_A_l = a->A_log_strides[0];
+  p.s_A_h = a->A_log_strides[1];
+  p.dt_bias = a->dt_bias;
+  p.s_dt_l = a->dt_bias_strides[0];
+  p.s_dt_h = a->dt_bias_strides[1];
+  p.s_dt_d = a->dt_bias_strides[2];
+  p.use_lb = a->use_lower_bound;
+  p.lb = a->lower_bound;
+  p.slots = a->state_indices;
+  p.commit_lens = a->commit_lens;
+  p.final_slots = a->final_state_indices;
+  p.record_rows = a->record_rows;
+  p.L = a->num_layers;
+  p.B = a->batch;
+  p.H = int32_t(H);
+  p.Q = int32_t(Q);
+  p.null_id = a->null_block_id;
+  p.N = a->num_slots;
+  p.R = a->num_record_rows;
+  p.kg_bf16 = a->key_gate_dtype == KDA_BF16;
+  plan->D = int(D);
+  plan->noop = a->batch == 0;
+  return KDA_OK;
+}
+
+int device_status(int hip_rc, const char* what) {
+  if (hip_rc == 0) return KDA_OK;
+  return fail(KDA_E_DEVICE, "%s: HIP error %d (%s)", what, hip_rc,
+              hipGetErrorString(hipError_t(hip_rc)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_last_error(void) { return g_err.c_str(); }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_E_SHAPE: return "KDA_E_SHAPE";
+    case KDA_E_DTYPE: return "KDA_E_DTYPE";
+    case KDA_E_LAYOUT: return "KDA_E_LAYOUT";
+    case KDA_E_UNALIGNED: return "KDA_E_UNALIGNED";
+    case KDA_E_UNSUPPORTED: return "KDA_E_UNSUPPORTED";
+    case KDA_E_CAPACITY: return "KDA_E_CAPACITY";
+    case KDA_E_DEVICE: return "KDA_E_DEVICE";
+    case KDA_E_ARG: return "KDA_E_ARG";
+    default: return "KDA_E_UNKNOWN";
+  }
+}
+
+int kda_check_verify(const kda_verify_args* args) {
+  g_err.clear();
+  VerifyPlan plan;
+  return plan_verify(args, &plan);
+}
+
+int kda_conv_update_verify(const kda_verify_args* args, void* stream) {
+  g_err.clear();
+  VerifyPlan plan;
+  KDA_TRY(plan_verify(args, &plan));
+  if (plan.noop) return KDA_OK;
+  return device_status(
+      kda::launch_verify(plan.p, plan.D, plan.act_bf16, plan.grid,
+                         static_cast<hipStream_t>(stream)),
+      "kda_conv_update_verify launch");
+}
+
+int kda_check_commit(const kda_commit_args* args) {
+  g_err.clear();
+  CommitPlan plan;
+  return plan_commit(args, &plan);
+}
+
+int kda_recoverssm_commit(const kda_commit_args* args, void* stream) {
+  g_err.clear();
+  CommitPlan plan;
+  KDA_TRY(plan_commit(args, &plan));
+  if (plan.noop) return KDA_OK;
+  return device_status(
+      kda::launch_commit(plan.p, plan.D, static_cast<hipStream_t>(stream)),
+      "kda_recoverssm_commit launch");
+}
+
+int kda_reset_counter(int32_t* counter, int32_t n, void* stream) {
+  g_err.clear();
+  if (counter == nullptr || n < 1)
+    return fail(KDA_E_ARG, "kda_reset_counter needs a counter and n >= 1");
+  return device_status(kda::launch_reset_counter(
+                           counter, n, static_cast<hipStream_t>(stream)),
+                       "kda_reset_counter launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+// Multi-layer RecoverSSM commit for gfx950: folds each request's first n
+// accepted draft positions into its fp32 checkpoint, for every KDA layer, in
+// one launch (kernels page `cute_recoverssm_commit`; ops page
+// `_commit_kda_state_kernel`, `KDARecoverSSMCommitContext.commit`).
+//
+// For one (layer, request, head), with the recorded correction c_t, raw key
+// k_t and raw gate of positions t < n:
+//   S_n = S_0 diag(Gam) + sum_{t<n} c_t (k_hat_t * Suf_t)^T
+//   Gam = prod_{t<n} d_t,   Suf_t = prod_{t<s<n} d_s,   d = exp(gate)
+// which is the n-step recurrence S <- S diag(d_t) + c_t k_hat_t^T written out.
+// The per-column vectors (Gam, k_hat_t * Suf_t) are built once per head in
+// LDS; each state element then costs 1 + n multiply-adds, so the kernel is a
+// streaming read-modify-write of the 64 KiB tile: 16-byte non-temporal
+// loads issued before the record work, stores to the final slot.
+//
+// One workgroup per (layer, request, head); blockIdx.x enumerates heads
+// fastest, so consecutive workgroups stream consecutive heads of one slot.
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace {
+
+template <int D, int QMAX>
+struct CommitCfg {
+  static constexpr int NT = D >= 128 ? 256 : (D == 64 ? 128 : 64);
+  static constexpr int L = D / 4;           // lanes per state row (float4)
+  static constexpr int RPP = NT / L;        // rows per pass
+  static constexpr int PASSES = D / RPP;
+  static constexpr int CW = (D + 63) / 64;  // waves holding columns
+  static constexpr int CS = QMAX + 4;       // padded row of corrections
+  static_assert(RPP * PASSES == D, "tile rows");
+};
+
+template <int D, int QMAX>
+struct alignas(16) CommitSmem {
+  using C = CommitCfg<D, QMAX>;
+  float w[QMAX][D];        // k_hat_t * Suf_t
+  float gam[D];            // Gam
+  float cT[D * C::CS];     // corrections, row v: c_0..c_{Q-1}
+  float red[C::CW][QMAX];  // wave partial sums of |k_t|^2
+};
+
+template <int D, int QMAX>
+__global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
+    kda_commit_kernel(CommitParams p) {
+  using C = CommitCfg<D, QMAX>;
+  __shared__ CommitSmem<D, QMAX> sm;
+  const int tid = threadIdx.x;
+  const int item = blockIdx.x;
+  const int per_layer = p.B * p.H;
+  const int l = uniform(item / per_layer);
+  const int rem = item - l * per_layer;
+  const int b = uniform(rem / p.H);
+  const int h = uniform(rem - b * p.H);
+
+  const int slot = p.slots[b];
+  if (slot <= p.null_id || slot < 0 || slot >= p.N) return;
+  const int n = min(max(p.commit_lens[b], 0), p.Q);
+  if (n == 0) return;
+  const int f = p.final_slots ? p.final_slots[b] : slot;
+  if (f <= p.null_id || f < 0 || f >= p.N) return;
+  const int r = p.record_rows ? p.record_rows[b] : slot;
+  if (r < 0 || r >= p.R) return;
+
+  float* state = reinterpret_cast<float*>(p.state_base[l]);
+  const int64_t sbs = p.state_bs[l];
+  const float* src = state + int64_t(slot) * sbs + int64_t(h) * p.s_state_head;
+  float* dst = state + int64_t(f) * sbs + int64_t(h) * p.s_state_head;
+
+  // Prefetch the whole tile: lane group rg owns rows rg, rg+RPP, ...
+  const int lg = tid % C::L, rg = tid / C::L;
+  const int col = 4 * lg;
+  f4 st[C::PASSES];
+#pragma unroll
+  for (int pp = 0; pp < C::PASSES; ++pp)
+    st[pp] = ld_stream(src + (pp * C::RPP + rg) * D + col);
+
+  // Records of this head.
+  const float* corr = reinterpret_cast<const float*>(p.corr_base[l]) +
+                      int64_t(r) * p.corr_bs[l] + int64_t(h) * p.s_c_head;
+  const int64_t kg_off = int64_t(r) * p.kg_bs[l] + int64_t(h) * p.s_kg_head;
+  const void* kg = reinterpret_cast<const void*>(p.kg_base[l]);
+  const bool kg_bf16 = p.kg_bf16 != 0;
+
+  // Corrections, transposed so that a row's values are contiguous.
+  for (int j = tid; j < QMAX * D; j += C::NT) {
+    const int t = j / D, v = j - t * D;
+    sm.cT[v * C::CS + t] = t < n ? corr[int64_t(t) * p.s_c_pos + v] : 0.0f;
+  }
+
+  // Per column k: raw keys and decays of the committed positions.
+  const float Ah = __expf(p.A_log[int64_t(l) * p.s_A_l + int64_t(h) * p.s_A_h]);
+  const bool use_lb = p.use_lb[l] != 0;
+  const float lb = p.lb[l];
+  const bool col_ok = tid < D;
+  const float bias =
+      col_ok ? p.dt_bias[int64_t(l) * p.s_dt_l + int64_t(h) * p.s_dt_h +
+                         int64_t(tid) * p.s_dt_d]
+             : 0.0f;
+  float kr[QMAX], dd[QMAX];
+#pragma unroll
+  for (int t = 0; t < QMAX; ++t) {
+    kr[t] = 0.0f;
+    dd[t] = 1.0f;
+    if (col_ok && t < n) {
+      const int64_t o = kg_off + int64_t(t) * p.s_kg_pos;
+      kr[t] = ld_elem(kg, o + tid, kg_bf16);
+      const float x = ld_elem(kg, o + D + tid, kg_bf16) + bias;
+      dd[t] = __expf(kda_gate(x, Ah, use_lb, lb));
+    }
+  }
+  const int wave = tid / 64, lane = tid % 64;
+  if (wave < C::CW) {
+#pragma unroll
+    for (int t = 0; t < QMAX; ++t) {
+      const float s = wave_sum(kr[t] * kr[t]);
+      if (lane == 0) sm.red[wave][t] = s;
+    }
+  }
+  lds_barrier();
+
+  if (col_ok) {
+    float suf = 1.0f;
+#pragma unroll
+    for (int t = QMAX - 1; t >= 0; --t) {
+      float sk = 0.0f;
+#pragma unroll
+      for (int w = 0; w < C::CW; ++w) sk += sm.red[w][t];
+      sm.w[t][tid] = kr[t] * rsqrtf(sk + kNormEps) * suf;
+      suf *= dd[t];
+    }
+    sm.gam[tid] = suf;
+  }
+  lds_barrier();
+
+  const f4 g4 = *reinterpret_cast<const f4*>(&sm.gam[col]);
+  f4 w4[QMAX];
+#pragma unroll
+  for (int t = 0; t < QMAX; ++t)
+    w4[t] = *reinterpret_cast<const f4*>(&sm.w[t][col]);
+#pragma unroll
+  for (int pp = 0; pp < C::PASSES; ++pp) {
+    const int row = pp * C::RPP + rg;
+    f4 acc = st[pp] * g4;
+    const float* cr = &sm.cT[row * C::CS];
+#pragma unroll
+    for (int t = 0; t < QMAX; ++t) {
+      if (t < n) {
+        const float c = cr[t];
+        acc.x = fmaf(c, w4[t].x, acc.x);
+        acc.y = fmaf(c, w4[t].y, acc.y);
+        acc.z = fmaf(c, w4[t].z, acc.z);
+        acc.w = fmaf(c, w4[t].w, acc.w);
+      }
+    }
+    st_stream(dst + row * D + col, acc);
+  }
+}
+
+template <int D, int QMAX>
+int launch_cq(const CommitParams& p, hipStream_t stream) {
+  using C = CommitCfg<D, QMAX>;
+  const int64_t items = int64_t(p.L) * p.B * p.H;
+  if (items > 0x7fffffff) return int(hipErrorInvalidValue);
+  hipLaunchKernelGGL((kda_commit_kernel<D, QMAX>), dim3(unsigned(items)),
+                     dim3(C::NT), 0, stream, p);
+  return int(hipGetLastError());
+}
+
+template <int D>
+int launch_cd(const CommitParams& p, hipStream_t stream) {
+  if (p.Q <= 4) return launch_cq<D, 4>(p, stream);
+  if (p.Q <= 8) return launch_cq<D, 8>(p, stream);
+  return launch_cq<D, 16>(p, stream);
+}
+
+}  // namespace
+
+int launch_commit(const CommitParams& p, int D, hipStream_t stream) {
+  switch (D) {
+    case 16: return launch_cd<16>(p, stream);
+    case 32: return launch_cd<32>(p, stream);
+    case 64: return launch_cd<64>(p, stream);
+    case 128: return launch_cd<128>(p, stream);
+    default: return int(hipErrorInvalidValue);
+  }
+}
+
+}  // namespace kda

@@ -1,0 +1,135 @@
+// Device-side helpers for the gfx950 KDA RecoverSSM kernels: bf16
+// conversion, cross-lane reductions with DPP, an LDS-only workgroup barrier,
+// streaming 16-byte memory ops and the KDA gate.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// ---- element conversion ------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(uint32_t(b) << 16);
+}
+
+// fp32 -> bf16 with round-to-nearest-even; NaNs stay NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ float ld_elem(const void* p, int64_t i, bool bf16) {
+  return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i])
+              : static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ void st_elem(void* p, int64_t i, float v,
+                                        bool bf16) {
+  if (bf16)
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+  else
+    static_cast<float*>(p)[i] = v;
+}
+
+template <bool BF16>
+struct Act;
+template <>
+struct Act<true> {
+  typedef uint16_t T;
+  static __device__ __forceinline__ float f(T x) { return bf16_to_f32(x); }
+};
+template <>
+struct Act<false> {
+  typedef float T;
+  static __device__ __forceinline__ float f(T x) { return x; }
+};
+
+// ---- streaming 16-byte accesses (state rows are touched once) -----------------
+
+__device__ __forceinline__ f4 ld_stream(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+}
+__device__ __forceinline__ void st_stream(float* p, f4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
+}
+
+// ---- synchronisation ---------------------------------------------------------
+
+// Workgroup barrier that orders LDS only.  Outstanding global loads (the
+// prefetched state tile) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---- cross-lane reductions ----------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// DPP control words (gfx9 encoding).
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <- 7-i within 8
+constexpr int kRowMirror = 0x140;      // lane i <- 15-i within 16
+
+// Sum over aligned groups of G consecutive lanes; every lane of a group
+// receives the group total.  Groups up to 16 use DPP only; 32 adds a
+// swizzle across the two halves of each 32-lane half-wave.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32,
+                "group size");
+  if constexpr (G >= 2) v += dpp<kQuadXor1>(v);
+  if constexpr (G >= 4) v += dpp<kQuadXor2>(v);
+  if constexpr (G >= 8) v += dpp<kRowHalfMirror>(v);
+  if constexpr (G >= 16) v += dpp<kRowMirror>(v);
+  if constexpr (G >= 32)
+    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v),
+                                                    0x401F));  // xor 16
+  return v;
+}
+
+// Sum over the whole 64-lane wave, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  const int b = __float_as_int(v);
+  return __int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(b, 16)) +
+         __int_as_float(__builtin_amdgcn_readlane(b, 32)) +
+         __int_as_float(__builtin_amdgcn_readlane(b, 48));
+}
+
+__device__ __forceinline__ int uniform(int x) {
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// ---- KDA math -------------------------------------------------------------------
+
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return 1.0f / (1.0f + __expf(-x));
+}
+
+// Log-decay of one channel from x = raw gate + dt_bias and A = exp(A_log):
+// bounded form lb * sigmoid(A x), else -A * softplus(x) where softplus is the
+// identity above 20 (ops page, `_kda_gate`).
+__device__ __forceinline__ float kda_gate(float x, float A, bool use_lb,
+                                          float lb) {
+  if (use_lb) return lb * sigmoidf_(A * x);
+  const float sp = x > 20.0f ? x : log1pf(__expf(x));
+  return -A * sp;
+}
+
+constexpr float kNormEps = 1e-6f;  // inside the square root of both norms
+
+}  // namespace kda

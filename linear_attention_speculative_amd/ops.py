@@ -1,0 +1,279 @@
+"""Python binding of the KDA RecoverSSM C ABI, taking torch tensors.
+
+Argument marshalling only: tensors are described by pointer, dtype, sizes and
+strides, and the current HIP stream is passed through.  Every step of the
+path runs in the HIP library; if it is missing these functions raise.
+
+Functions mirror the pages' host API:
+  * `conv_update_verify` -- the kernels page's `CuteRecoverSSMVerify.__call__`
+    (fused conv update + verify), with the ops page's record layout;
+  * `CommitContext` -- the ops page's `KDARecoverSSMCommitContext` (per-layer
+    address tables built once, then one commit launch per step).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _abi
+
+_DT = {torch.float32: _abi.KDA_F32, torch.bfloat16: _abi.KDA_BF16}
+
+
+class KdaError(RuntimeError):
+    """A failing library call: `status` is the kda_status code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class KdaUnaligned(KdaError):
+    """An activation is not 16-byte aligned; nothing was launched."""
+
+
+def _status_name(code: int) -> str:
+    return _abi.load().kda_status_string(code).decode()
+
+
+def _raise(code: int):
+    msg = _abi.load().kda_last_error().decode()
+    cls = KdaUnaligned if code == _abi.KDA_E_UNALIGNED else KdaError
+    raise cls(code, msg)
+
+
+def describe(t: Optional[torch.Tensor]) -> _abi.KdaTensor:
+    """Descriptor of a tensor view (sizes and strides in elements)."""
+    d = _abi.KdaTensor()
+    if t is None:
+        return d
+    if t.dim() > 4:
+        raise ValueError("tensors of at most 4 dimensions")
+    d.data = t.data_ptr()
+    d.dtype = _DT.get(t.dtype, -1)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if t.dtype != torch.int32:
+        raise TypeError("metadata tensors must be int32")
+    if not t.is_contiguous():
+        raise ValueError("metadata tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
+                lower_bound, state, correction, key_gate, out, conv_state,
+                conv_weight, query_start_loc, state_indices,
+                num_accepted_tokens, spec_query_len, conv_dim_first,
+                work_counter, record_rows=None, null_block_id=0,
+                max_workgroups=0) -> _abi.KdaVerifyArgs:
+    a = _abi.KdaVerifyArgs()
+    a.mixed_qkv = describe(mixed_qkv)
+    a.raw_gate = describe(raw_gate)
+    a.raw_beta = describe(raw_beta)
+    a.A_log = describe(A_log)
+    a.dt_bias = describe(dt_bias)
+    a.state = describe(state)
+    a.correction = describe(correction)
+    a.key_gate = describe(key_gate)
+    a.out = describe(out)
+    a.conv_state = describe(conv_state)
+    a.conv_weight = describe(conv_weight)
+    a.query_start_loc = _ptr(query_start_loc)
+    a.state_indices = _ptr(state_indices)
+    a.num_accepted_tokens = _ptr(num_accepted_tokens)
+    a.record_rows = _ptr(record_rows)
+    a.work_counter = _ptr(work_counter)
+    a.batch = state_indices.shape[0]
+    a.spec_query_len = spec_query_len
+    a.null_block_id = null_block_id
+    a.conv_dim_first = 1 if conv_dim_first else 0
+    a.use_lower_bound = 0 if lower_bound is None else 1
+    a.lower_bound = 0.0 if lower_bound is None else float(lower_bound)
+    a.max_workgroups = max_workgroups
+    return a
+
+
+def check_verify(**kwargs) -> int:
+    """Host-only validation (no launch); returns the kda_status code."""
+    a = verify_args(**kwargs)
+    return _abi.load().kda_check_verify(ctypes.byref(a))
+
+
+def conv_update_verify(*, stream=None, **kwargs) -> None:
+    """Fused conv update + speculative verify of one KDA layer on the current
+    (or given) stream.  Arguments follow kda_verify_args in
+    include/kda_recoverssm.h; `lower_bound=None` selects the softplus gate.
+    Raises KdaUnaligned (nothing launched) for misaligned activations and
+    KdaError for any other rejected argument."""
+    a = verify_args(**kwargs)
+    rc = _abi.load().kda_conv_update_verify(ctypes.byref(a),
+                                           _stream(stream))
+    if rc != _abi.KDA_OK:
+        _raise(rc)
+
+
+def reset_counter(counter: torch.Tensor, stream=None) -> None:
+    rc = _abi.load().kda_reset_counter(_ptr(counter), counter.numel(),
+                                      _stream(stream))
+    if rc != _abi.KDA_OK:
+        _raise(rc)
+
+
+def abi_version() -> int:
+    return _abi.load().kda_abi_version()
+
+
+class CommitContext:
+    """Per-layer address tables and stacked gate parameters for the
+    multi-layer commit, built once (ops page,
+    `KDARecoverSSMCommitContext.create`), then `commit` per step.
+
+    `layers` is a sequence of dicts with `state` [N,H,D,D] f32,
+    `correction` [R,H,Q,D] f32, `key_gate` [R,H,Q,2D], `A_log` [H],
+    `dt_bias` [H,D] (or [H*D]) and `lower_bound` (None = softplus).
+    Every layer must share sizes, dtypes and inner strides; slot strides
+    may differ per layer.
+    """
+
+    def __init__(self, layers: Sequence[dict], *, spec_query_len: int,
+                 null_block_id: int = 0):
+        if not layers:
+            raise ValueError("KDA RecoverSSM commit requires at least one "
+                             "layer")
+        ref = layers[0]
+        st, corr, kg = ref["state"], ref["correction"], ref["key_gate"]
+        if st.dim() != 4:
+            raise ValueError("KDA RecoverSSM checkpoint must be "
+                             "four-dimensional")
+        N, H, V, K = st.shape
+        if V != K:
+            raise ValueError("key and value head dims must be equal")
+        Q = spec_query_len
+        for L in layers:
+            s = L["state"]
+            if (s.shape != st.shape or s.dtype != torch.float32 or
+                    s.device != st.device or s.stride()[1:] != st.stride()[1:]):
+                raise ValueError("KDA RecoverSSM layers need matching "
+                                 "checkpoint layout")
+            c = L["correction"]
+            if (c.shape[1:] != (H, Q, V) or c.shape[0] != corr.shape[0] or
+                    c.dtype != torch.float32 or c.device != st.device or
+                    c.stride()[1:] != corr.stride()[1:]):
+                raise ValueError("KDA RecoverSSM correction buffers need "
+                                 f"float32 shape [rows, {H}, {Q}, {V}]")
+            g = L["key_gate"]
+            if (g.shape != (c.shape[0], H, Q, 2 * K) or g.dtype != kg.dtype or
+                    g.device != st.device or g.stride()[1:] != kg.stride()[1:]):
+                raise ValueError("KDA RecoverSSM key/gate buffers need shape "
+                                 f"[rows, {H}, {Q}, {2 * K}]")
+            if L["A_log"].shape != (H,):
+                raise ValueError("KDA RecoverSSM A_log shape is incompatible")
+            if L["dt_bias"].numel() != H * K:
+                raise ValueError("KDA RecoverSSM dt_bias shape is "
+                                 "incompatible")
+        dev = st.device
+        self.layers = list(layers)
+        self.num_layers = len(layers)
+        self.H, self.D, self.Q, self.N = H, K, Q, N
+        self.R = corr.shape[0]
+        self.null_block_id = null_block_id
+        self.key_gate_dtype = _DT[kg.dtype]
+        self.state_strides = st.stride()[1:3]
+        self.correction_strides = corr.stride()[1:3]
+        self.key_gate_strides = kg.stride()[1:3]
+
+        def col(key, fn):
+            return [fn(L[key]) for L in layers]
+
+        host = torch.tensor(
+            [col("state", lambda t: t.data_ptr()),
+             col("state", lambda t: t.stride(0)),
+             col("correction", lambda t: t.data_ptr()),
+             col("correction", lambda t: t.stride(0)),
+             col("key_gate", lambda t: t.data_ptr()),
+             col("key_gate", lambda t: t.stride(0))], dtype=torch.int64)
+        self._host_tables = host.contiguous()
+        self.tables = self._host_tables.to(dev)
+        self.A_log = torch.stack([L["A_log"].float() for L in layers]) \
+            .contiguous().to(dev)
+        self.dt_bias = torch.stack(
+            [L["dt_bias"].float().reshape(H, K) for L in layers]) \
+            .contiguous().to(dev)
+        self.use_lower_bound = torch.tensor(
+            [0 if L.get("lower_bound") is None else 1 for L in layers],
+            dtype=torch.int32, device=dev)
+        self.lower_bound = torch.tensor(
+            [0.0 if L.get("lower_bound") is None else float(L["lower_bound"])
+             for L in layers], dtype=torch.float32, device=dev)
+
+    def args(self, state_indices, commit_lens, final_state_indices=None,
+             record_rows=None) -> _abi.KdaCommitArgs:
+        a = _abi.KdaCommitArgs()
+        a.num_layers = self.num_layers
+        a.batch = state_indices.shape[0]
+        a.num_heads = self.H
+        a.head_dim = self.D
+        a.spec_query_len = self.Q
+        a.null_block_id = self.null_block_id
+        a.num_slots = self.N
+        a.num_record_rows = self.R
+        base = self.tables.data_ptr()
+        L8 = self.num_layers * 8
+        a.state_base_addrs = base
+        a.state_block_strides = base + L8
+        a.correction_base_addrs = base + 2 * L8
+        a.correction_block_strides = base + 3 * L8
+        a.key_gate_base_addrs = base + 4 * L8
+        a.key_gate_block_strides = base + 5 * L8
+        a.state_strides[:] = list(self.state_strides)
+        a.correction_strides[:] = list(self.correction_strides)
+        a.key_gate_strides[:] = list(self.key_gate_strides)
+        a.key_gate_dtype = self.key_gate_dtype
+        a.A_log = self.A_log.data_ptr()
+        a.A_log_strides[:] = list(self.A_log.stride())
+        a.dt_bias = self.dt_bias.data_ptr()
+        a.dt_bias_strides[:] = list(self.dt_bias.stride())
+        a.use_lower_bound = self.use_lower_bound.data_ptr()
+        a.lower_bound = self.lower_bound.data_ptr()
+        a.state_indices = _ptr(state_indices)
+        a.commit_lens = _ptr(commit_lens)
+        a.final_state_indices = _ptr(final_state_indices)
+        a.record_rows = _ptr(record_rows)
+        a.host_tables = self._host_tables.numpy().ctypes.data_as(
+            ctypes.POINTER(ctypes.c_int64))
+        return a
+
+    def check(self, state_indices, commit_lens, final_state_indices=None,
+              record_rows=None) -> int:
+        a = self.args(state_indices, commit_lens, final_state_indices,
+                      record_rows)
+        return _abi.load().kda_check_commit(ctypes.byref(a))
+
+    def commit(self, state_indices, commit_lens, final_state_indices=None,
+               record_rows=None, stream=None) -> None:
+        """Fold the first commit_lens[b] recorded positions of every request
+        into its checkpoint (or final slot), for all layers, in one launch."""
+        a = self.args(state_indices, commit_lens, final_state_indices,
+                      record_rows)
+        rc = _abi.load().kda_recoverssm_commit(ctypes.byref(a),
+                                              _stream(stream))
+        if rc != _abi.KDA_OK:
+            _raise(rc)

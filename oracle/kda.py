@@ -16,7 +16,8 @@ Readings taken where the pages are silent (each is listed in the design doc):
   * Records go to `record_rows[b]` when given, else to the request's state
     slot; a negative or out-of-range row means "write no records" (verify)
     and "skip" (commit).
-  * q_b is clamped to [0, Q], accepted to [1, Q], commit length to [0, Q].
+  * q_b is clamped to [0, Q], accepted to [1, Q], commit length to [0, Q];
+    token rows outside [0, T) are never touched; negative slots are null.
 """
 from __future__ import annotations
 
@@ -132,7 +133,8 @@ def conv_update_verify(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
                        conv_weight, query_start_loc, state_indices,
                        num_accepted_tokens, spec_query_len, null_block_id=0,
                        use_lower_bound=False, lower_bound=0.0,
-                       record_rows=None, key_gate_dtype="f32", heads=None):
+                       record_rows=None, key_gate_dtype="f32", heads=None,
+                       requests=None):
     """Speculative verify of one KDA layer with the short conv fused in.
 
     Follows the ops page's `_kda_recoverssm_verify_kernel` (per request and
@@ -144,7 +146,9 @@ def conv_update_verify(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
     Array arguments are float64 (exact widenings); `conv_state` is the
     dim-first logical view [N, 3HK, Lc].  Returns a dict of updated copies
     `out`, `correction`, `key_gate`, `conv_state` and masks `out_written`
-    [T, HV] and `rec_written` [R, H, Q].
+    [T, HV] and `rec_written` [R, H, Q].  `heads` / `requests` restrict the
+    work to a sample (for checking large workloads); requests are
+    independent, so a sample's results equal the full run's.
     """
     Q = int(spec_query_len)
     N, H, V, K = state.shape
@@ -159,13 +163,16 @@ def conv_update_verify(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
     rec_written = np.zeros(correction.shape[:3], dtype=bool)
     hs = np.arange(H) if heads is None else np.asarray(heads)
     qsl = np.asarray(query_start_loc)
-    for b in range(len(state_indices)):
+    bs = range(len(state_indices)) if requests is None else requests
+    T = out.shape[0]
+    for b in bs:
         bos = int(qsl[b])
-        q = min(max(int(qsl[b + 1]) - bos, 0), Q)
+        q = 0 if (bos < 0 or bos >= T) else \
+            min(max(int(qsl[b + 1]) - bos, 0), Q, T - bos)
         if q == 0:
             continue
         slot = int(state_indices[b])
-        if slot <= null_block_id or slot >= N:
+        if slot <= null_block_id or slot < 0 or slot >= N:
             out[bos:bos + q, :] = 0.0
             out_written[bos:bos + q, :] = True
             continue
@@ -203,7 +210,7 @@ def conv_update_verify(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
 
 def commit(*, layers, state_indices, commit_lens, spec_query_len,
            null_block_id=0, final_state_indices=None, record_rows=None,
-           heads=None):
+           heads=None, requests=None):
     """Fold each request's first n accepted positions into its checkpoint,
     for every layer (ops page, `_commit_kda_state_kernel` and
     `KDARecoverSSMCommitContext.commit`; kernels page,
@@ -218,7 +225,7 @@ def commit(*, layers, state_indices, commit_lens, spec_query_len,
     `layers` is a list of dicts with float64 `state` [N,H,V,K], `correction`
     [R,H,Q,V], `key_gate` [R,H,Q,2K], `A_log` [H], `dt_bias` [H,K] and
     `use_lower_bound`, `lower_bound`.  Returns a list of (new state, written
-    mask [N, H]).
+    mask [N, H]).  `heads` / `requests` restrict the work to a sample.
     """
     Q = int(spec_query_len)
     results = []
@@ -231,16 +238,17 @@ def commit(*, layers, state_indices, commit_lens, spec_query_len,
         new = np.array(state, dtype=np.float64, copy=True)
         written = np.zeros((N, H), dtype=bool)
         hs = np.arange(H) if heads is None else np.asarray(heads)
-        for b in range(len(state_indices)):
+        bs = range(len(state_indices)) if requests is None else requests
+        for b in bs:
             slot = int(state_indices[b])
-            if slot <= null_block_id or slot >= N:
+            if slot <= null_block_id or slot < 0 or slot >= N:
                 continue
             n = min(max(int(commit_lens[b]), 0), Q)
             if n == 0:
                 continue
             f = slot if final_state_indices is None \
                 else int(final_state_indices[b])
-            if f <= null_block_id or f >= N:
+            if f <= null_block_id or f < 0 or f >= N:
                 continue
             r = int(record_rows[b]) if record_rows is not None else slot
             if not 0 <= r < R:

@@ -1,0 +1,140 @@
+"""Helpers of the GPU parity tests: capture the oracle inputs of a sample of
+requests before a launch, run the fp64 oracle on a compact copy of them, and
+compare what the HIP path wrote.
+
+Comparison rule (one number per tensor): err = max|gpu - ref| / max|ref|
+over the written region, at most 2e-3 for bf16 activations and 1e-4 for
+fp32 inputs.  Copies (conv-state roll, raw-gate record half), null outputs
+and every byte that must not change are compared bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from workloads.sample import Sample, f64, snapshot  # noqa: F401
+
+TOL = {"f32": 1e-4, "bf16": 2e-3}
+
+
+def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    if ref.size == 0:
+        return 0.0
+    scale = float(np.max(np.abs(ref)))
+    diff = float(np.max(np.abs(np.asarray(gpu, np.float64) - ref)))
+    return diff / scale if scale > 0 else diff
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bit patterns (for bitwise comparisons, NaN-safe)."""
+    t = t.detach().contiguous().to("cpu")
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy()
+    return t.numpy()
+
+
+def run_oracle_verify(sample: Sample, inputs: dict = None) -> dict:
+    return oracle.conv_update_verify(**(inputs or sample.inputs))
+
+
+def check_verify(wl, layer: int, sample: Sample, ref: dict,
+                 kg_k_tol: float = None) -> dict:
+    """Compare the GPU tensors of `layer` (after the verify launch) with the
+    oracle results `ref` for the sample.  Returns the measured errors."""
+    L = wl.layers[layer]
+    tol = TOL[wl.act]
+    errs = {}
+    dev = L.state.device
+    tok_all = [t for ts in sample.tok for t in ts]
+    Q, D = wl.Q, wl.D
+
+    # outputs
+    if tok_all:
+        out = L.out.index_select(0, torch.tensor(tok_all, device=dev))
+        out_gpu = f64(out)
+        out_bits = bits(out)
+        m = ref["out_written"]
+        live_rows, null_rows = [], []
+        k = 0
+        for i, ts in enumerate(sample.tok):
+            q = min(len(ts), Q)
+            rows = list(range(k, k + q))
+            (live_rows if sample.valid[i] else null_rows).extend(rows)
+            k += len(ts)
+        if live_rows:
+            lr = np.array(live_rows)
+            assert m[lr].all()
+            errs["out"] = rel_err(out_gpu[lr], ref["out"][lr])
+            assert errs["out"] <= tol, ("out", errs["out"])
+        if null_rows:
+            nb = out_bits[np.array(null_rows)]
+            assert np.all(nb == 0), "null outputs must be +0.0"
+
+    # conv state roll: bitwise
+    live = [i for i, ok in enumerate(sample.valid) if ok]
+    if live:
+        oslots = torch.tensor([int(sample.slots[i]) for i in live], device=dev)
+        conv_gpu = f64(wl.conv_state_dim_first(layer).index_select(0, oslots))
+        conv_ref = ref["conv_state"][[int(sample.new_slot[i]) for i in live]]
+        assert np.array_equal(conv_gpu, conv_ref), "conv state roll mismatch"
+
+    # records
+    rec = [(i, int(sample.rows[i]), int(sample.new_row[i])) for i in live
+           if sample.rows[i] >= 0]
+    if rec:
+        ridx = torch.tensor([r for _, r, _ in rec], device=dev)
+        corr_gpu = f64(L.correction.index_select(0, ridx))
+        kg_t = L.key_gate.index_select(0, ridx)
+        kg_gpu = f64(kg_t)
+        nr = [n for _, _, n in rec]
+        corr_ref = ref["correction"][nr]
+        kg_ref = ref["key_gate"][nr]
+        w = ref["rec_written"][nr]                      # [n, H, Q]
+        wc = np.broadcast_to(w[..., None], corr_ref.shape)
+        errs["correction"] = rel_err(corr_gpu[wc], corr_ref[wc])
+        assert errs["correction"] <= tol, ("correction", errs["correction"])
+        # unwritten positions keep their bytes (ref holds the inputs there)
+        assert np.array_equal(corr_gpu[~wc], corr_ref[~wc])
+        wk = np.broadcast_to(w[..., None], kg_ref[..., :D].shape)
+        kt = kg_k_tol if kg_k_tol is not None else tol
+        errs["key"] = rel_err(kg_gpu[..., :D][wk], kg_ref[..., :D][wk])
+        assert errs["key"] <= kt, ("key record", errs["key"])
+        assert np.array_equal(kg_gpu[..., D:], kg_ref[..., D:]), \
+            "raw gate record half must be an exact copy"
+        assert np.array_equal(kg_gpu[..., :D][~wk], kg_ref[..., :D][~wk])
+    return errs
+
+
+def commit_layer_inputs(sample: Sample, ref: dict, L) -> dict:
+    """Oracle commit inputs of one layer: the checkpoint the sample was
+    taken from and the records the oracle's verify produced."""
+    return dict(state=sample.inputs["state"], correction=ref["correction"],
+                key_gate=ref["key_gate"], A_log=sample.inputs["A_log"],
+                dt_bias=sample.inputs["dt_bias"],
+                use_lower_bound=L.use_lower_bound,
+                lower_bound=L.lower_bound)
+
+
+def check_commit(wl, layer: int, sample: Sample, new_state: np.ndarray,
+                 written: np.ndarray, final_slots=None) -> float:
+    """Compare the GPU checkpoint of `layer` after the commit with the
+    oracle's committed states of the sample (compact pool)."""
+    L = wl.layers[layer]
+    dev = L.state.device
+    idx, cidx = [], []
+    for i, ok in enumerate(sample.valid):
+        ns = int(sample.new_slot[i])
+        if ok and written[ns].any():
+            dst = int(sample.slots[i]) if final_slots is None \
+                else int(final_slots[sample.reqs[i]])
+            idx.append(dst)
+            cidx.append(ns)
+    if not idx:
+        return 0.0
+    gpu = f64(L.state.index_select(0, torch.tensor(idx, device=dev)))
+    err = rel_err(gpu, new_state[cidx])
+    assert err <= TOL[wl.act], ("committed state", err)
+    return err

@@ -1,0 +1,231 @@
+"""The C-ABI library loads without a GPU, exports every function the header
+declares, and its host-only checks map each rule of the pages' validation
+to its status code (no launch, no device memory: descriptors point at CPU
+tensors that are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import linear_attention_speculative_amd as kda
+from linear_attention_speculative_amd import _abi
+from workloads import make_workload
+from workloads.drive import verify_kwargs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda_recoverssm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = _abi.load()
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert set(declared) == set(_abi.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert kda.abi_version() == 1
+    assert lib.kda_status_string(_abi.KDA_E_UNALIGNED) == b"KDA_E_UNALIGNED"
+
+
+def _kw(**over):
+    wl = make_workload(over.pop("cfg", "ragged"), B=4, H=2, D=16, Q=4, N=8,
+                       **over)
+    counter = torch.zeros(1, dtype=torch.int32)
+    return wl, verify_kwargs(wl, 0, counter)
+
+
+def _code(kw):
+    return kda.check_verify(**kw)
+
+
+def test_valid_arguments_pass_both_layouts_and_dtypes():
+    for dim_first in (True, False):
+        for act in ("f32", "bf16"):
+            for out_dtype in ("f32", "act"):
+                for kg in ("f32", "act"):
+                    wl, kw = _kw(conv_dim_first=dim_first, act=act,
+                                 weight=act, out_dtype=out_dtype,
+                                 kg_dtype=kg)
+                    assert _code(kw) == 0, kda.load().kda_last_error()
+
+
+def test_tiny_and_deferred_configs_pass():
+    wl = make_workload("tiny")
+    assert _code(verify_kwargs(wl, 0, torch.zeros(1, dtype=torch.int32))) == 0
+    wl = make_workload("deferred", B=8, H=2, D=32, N=16)
+    for layer in range(2):
+        assert _code(verify_kwargs(wl, layer,
+                                   torch.zeros(1, dtype=torch.int32))) == 0
+
+
+def test_shape_errors():
+    wl, kw = _kw()
+    kw["raw_gate"] = kw["raw_gate"][:, :-8]
+    assert _code(kw) == _abi.KDA_E_SHAPE
+    wl, kw = _kw()
+    kw["out"] = torch.empty(wl.T, wl.H * wl.D + 4)
+    assert _code(kw) == _abi.KDA_E_SHAPE
+    wl, kw = _kw()
+    kw["A_log"] = torch.zeros(wl.H + 1)
+    assert _code(kw) == _abi.KDA_E_SHAPE
+    wl, kw = _kw()
+    kw["correction"] = kw["correction"][:, :, :2]
+    assert _code(kw) == _abi.KDA_E_SHAPE
+    wl, kw = _kw()
+    kw["conv_weight"] = torch.zeros(3 * wl.H * wl.D, 3)
+    assert _code(kw) == _abi.KDA_E_SHAPE
+
+
+def test_dtype_errors():
+    wl, kw = _kw(act="bf16", weight="bf16")
+    kw["raw_beta"] = kw["raw_beta"].float()
+    assert _code(kw) == _abi.KDA_E_DTYPE
+    wl, kw = _kw()
+    kw["correction"] = torch.zeros(kw["correction"].shape,
+                                   dtype=torch.bfloat16)
+    assert _code(kw) == _abi.KDA_E_DTYPE
+    wl, kw = _kw()
+    kw["state"] = torch.zeros(kw["state"].shape, dtype=torch.bfloat16)
+    assert _code(kw) == _abi.KDA_E_DTYPE
+    wl, kw = _kw()
+    kw["mixed_qkv"] = kw["mixed_qkv"].half()
+    assert _code(kw) == _abi.KDA_E_DTYPE
+
+
+def test_layout_errors_on_static_tensors():
+    wl, kw = _kw()
+    st = kw["state"]
+    kw["state"] = st.transpose(2, 3)   # heads no longer row-major
+    assert _code(kw) == _abi.KDA_E_LAYOUT
+    wl, kw = _kw()
+    # a slot stride that is not a multiple of 16 bytes
+    big = torch.zeros(wl.N * (wl.H * wl.D * wl.D + 1))
+    kw["state"] = big.as_strided((wl.N, wl.H, wl.D, wl.D),
+                                 (wl.H * wl.D * wl.D + 1, wl.D * wl.D, wl.D, 1))
+    assert _code(kw) == _abi.KDA_E_LAYOUT
+    wl, kw = _kw()
+    buf = torch.zeros(kw["conv_weight"].numel() + 1)
+    kw["conv_weight"] = buf[1:].view(kw["conv_weight"].shape)  # 4-byte offset
+    assert _code(kw) == _abi.KDA_E_LAYOUT
+
+
+def test_unaligned_activation_is_reported_without_launch():
+    wl, kw = _kw()
+    x = kw["mixed_qkv"]
+    buf = torch.zeros(x.shape[0] * x.shape[1] + 1, dtype=x.dtype)
+    kw["mixed_qkv"] = buf[1:].view(x.shape)    # one element past 16 bytes
+    assert _code(kw) == _abi.KDA_E_UNALIGNED
+    wl, kw = _kw()
+    x = kw["out"]
+    wide = torch.zeros(x.shape[0], x.shape[1] + 1, dtype=x.dtype)
+    kw["out"] = wide[:, :x.shape[1]]           # row stride not 16-byte
+    assert _code(kw) == _abi.KDA_E_UNALIGNED
+    # the launch entry point refuses it the same way, before any device work
+    with pytest.raises(kda.KdaUnaligned):
+        kda.conv_update_verify(stream=0, **kw)
+
+
+def test_unsupported_sizes():
+    wl, kw = _kw()
+    kw["spec_query_len"] = 17
+    assert _code(kw) == _abi.KDA_E_UNSUPPORTED
+    wl = make_workload("ragged", B=2, H=1, D=8, Q=4, N=4)
+    kw = verify_kwargs(wl, 0, torch.zeros(1, dtype=torch.int32))
+    assert _code(kw) == _abi.KDA_E_UNSUPPORTED            # head dim 8
+    wl, kw = _kw()
+    cs = kw["conv_state"]
+    kw["conv_state"] = cs[:, :, :-1]                      # width-3 conv
+    assert _code(kw) == _abi.KDA_E_UNSUPPORTED
+
+
+def test_capacity_and_argument_errors():
+    wl, kw = _kw()
+    kw["spec_query_len"] = 1
+    kw["correction"] = kw["correction"][:, :, :1]
+    kw["key_gate"] = kw["key_gate"][:, :, :1]
+    kw["conv_state"] = torch.zeros(wl.N, 3 * wl.H * wl.D, 3,
+                                   dtype=kw["conv_state"].dtype)
+    assert _code(kw) == _abi.KDA_E_CAPACITY
+    wl, kw = _kw()
+    kw["work_counter"] = None
+    assert _code(kw) == _abi.KDA_E_ARG
+
+
+def test_zero_batch_is_a_valid_no_op():
+    wl, kw = _kw()
+    for k in ("mixed_qkv", "raw_gate", "raw_beta", "out"):
+        kw[k] = kw[k][:0]
+    kw["state_indices"] = kw["state_indices"][:0]
+    kw["query_start_loc"] = kw["query_start_loc"][:1]
+    kw["num_accepted_tokens"] = kw["num_accepted_tokens"][:0]
+    assert _code(kw) == 0
+    kda.conv_update_verify(stream=0, **kw)   # returns without launching
+
+
+def _commit_ctx(**over):
+    wl = make_workload(over.pop("cfg", "large"), B=4, H=2, D=16, Q=8, N=8,
+                       gates=[None, -5.0, None], **over)
+    layers = [dict(state=L.state, correction=L.correction,
+                   key_gate=L.key_gate, A_log=L.A_log, dt_bias=L.dt_bias,
+                   lower_bound=L.lower_bound if L.use_lower_bound else None)
+              for L in wl.layers]
+    return wl, layers
+
+
+def test_commit_context_checks():
+    wl, layers = _commit_ctx()
+    # device tables on the CPU here: only the host-side checks run
+    ctx = kda.CommitContext(layers, spec_query_len=wl.Q)
+    assert ctx.check(wl.state_indices, wl.commit_lens) == 0
+    assert ctx.check(wl.state_indices, wl.commit_lens,
+                     final_state_indices=wl.state_indices) == 0
+    with pytest.raises(ValueError):
+        kda.CommitContext([], spec_query_len=wl.Q)
+    bad = dict(layers[1])
+    bad["state"] = bad["state"][:, :, :, :8]
+    with pytest.raises(ValueError):
+        kda.CommitContext([layers[0], bad], spec_query_len=wl.Q)
+    bad = dict(layers[1])
+    bad["key_gate"] = bad["key_gate"][:, :, :4]
+    with pytest.raises(ValueError):
+        kda.CommitContext([layers[0], bad], spec_query_len=wl.Q)
+
+
+def test_commit_abi_codes():
+    wl, layers = _commit_ctx()
+    ctx = kda.CommitContext(layers, spec_query_len=wl.Q)
+    lib = kda.load()
+
+    def code(mut):
+        a = ctx.args(wl.state_indices, wl.commit_lens)
+        mut(a)
+        return lib.kda_check_commit(ctypes.byref(a))
+
+    assert code(lambda a: None) == 0
+    assert code(lambda a: setattr(a, "num_layers", 0)) == _abi.KDA_E_ARG
+    assert code(lambda a: setattr(a, "head_dim", 48)) == \
+        _abi.KDA_E_UNSUPPORTED
+    assert code(lambda a: setattr(a, "spec_query_len", 0)) == \
+        _abi.KDA_E_UNSUPPORTED
+    assert code(lambda a: a.state_strides.__setitem__(1, 17)) == \
+        _abi.KDA_E_LAYOUT
+    assert code(lambda a: setattr(a, "key_gate_dtype", 7)) == \
+        _abi.KDA_E_DTYPE
+    assert code(lambda a: setattr(a, "commit_lens", None)) == _abi.KDA_E_ARG
+    # a misaligned layer base in the host copy of the tables
+    host = ctx._host_tables.clone()
+    host[0, 1] += 4
+    keep = host.numpy()
+
+    def mis(a):
+        a.host_tables = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    assert code(mis) == _abi.KDA_E_LAYOUT
+    assert b"layer 1" in lib.kda_last_error()

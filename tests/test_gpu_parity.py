@@ -1,0 +1,368 @@
+"""Parity of the HIP verify/commit (called through the C ABI) with the fp64
+oracle on seeded inputs: the small workload in full, the single-request and
+ragged workloads in full, the multi-layer, deferred and headline workloads at
+their full sizes on sampled requests, plus edge cases, sweeps over head dims
+and windows, determinism across grid sizes, the ticket counter protocol and
+HIP-graph replay."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_speculative_amd as kda
+import oracle
+from tests.gpu_check import (TOL, bits, check_commit, check_verify,
+                             commit_layer_inputs, f64, rel_err,
+                             run_oracle_verify, snapshot)
+from workloads import drive, make_workload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _counter():
+    return torch.zeros(1, dtype=torch.int32, device=DEV)
+
+
+def _view_mask(wl, record_page=False):
+    """Bool mask over a page row: True inside a tensor view."""
+    L = wl.layers[0]
+    page = L.record_page if record_page else L.page
+    m = torch.zeros(page.shape[1], dtype=torch.bool, device=page.device)
+    views = wl.meta["page_views"]
+    names = ("correction", "key_gate") if record_page else \
+        (("conv", "state") + (("correction", "key_gate")
+                              if wl.meta["records_in_page"] else ()))
+    for nm in names:
+        off, n = views[nm]
+        m[off:off + n] = True
+    return m
+
+
+def _check_pages(wl, layer, page_before, rec_before=None):
+    """Pages of slots no live request names are bitwise unchanged; padding
+    bytes of every page are unchanged."""
+    L = wl.layers[layer]
+    slots = wl.state_indices.cpu().numpy()
+    live = sorted({int(s) for s in slots if 0 < s < wl.N})
+    unused = torch.ones(wl.N, dtype=torch.bool, device=DEV)
+    if live:
+        unused[torch.tensor(live, device=DEV)] = False
+    assert torch.equal(L.page[unused], page_before[unused])
+    pad = ~_view_mask(wl)
+    assert torch.equal(L.page[:, pad], page_before[:, pad])
+    if rec_before is not None:
+        pad = ~_view_mask(wl, record_page=True)
+        assert torch.equal(L.record_page[:, pad], rec_before[:, pad])
+        rows = wl.record_rows.cpu().numpy()
+        used = {int(rows[b]) for b in range(wl.B) if 0 < slots[b] < wl.N}
+        keep = torch.tensor([r not in used for r in range(wl.R)], device=DEV)
+        assert torch.equal(L.record_page[keep], rec_before[keep])
+
+
+def _verify_case(wl, layer=0, reqs=None, max_wg=0, kg_tol=None):
+    L = wl.layers[layer]
+    sample = snapshot(wl, layer, reqs)
+    state_before = L.state.clone()
+    page_before = L.page.clone()
+    rec_before = None if L.record_page is None else L.record_page.clone()
+    counter = _counter()
+    drive.verify(wl, layer, counter, max_workgroups=max_wg)
+    torch.cuda.synchronize()
+    assert int(counter.item()) == 0, "ticket counter must be left at 0"
+    assert torch.equal(L.state, state_before), "verify wrote the checkpoint"
+    ref = run_oracle_verify(sample)
+    errs = check_verify(wl, layer, sample, ref, kg_k_tol=kg_tol)
+    _check_pages(wl, layer, page_before, rec_before)
+    return sample, ref, errs
+
+
+def _commit_case(wl, samples_refs, layers=None, final=None, lens=None):
+    """Run the GPU commit over `layers` and compare with the oracle commit of
+    each sampled layer.  samples_refs: {layer: (sample, ref)}."""
+    ctx = drive.commit_context(wl, layers)
+    lens_t = wl.commit_lens if lens is None else lens
+    before = {l: wl.layers[l].state.clone() for l in samples_refs}
+    ctx.commit(wl.state_indices, lens_t, final_state_indices=final,
+               record_rows=wl.record_rows)
+    torch.cuda.synchronize()
+    errs = {}
+    lens_np = lens_t.cpu().numpy()
+    for l, (sample, ref) in samples_refs.items():
+        L = wl.layers[l]
+        (new, written), = oracle.commit(
+            layers=[commit_layer_inputs(sample, ref, L)],
+            state_indices=sample.new_slot, commit_lens=lens_np[sample.reqs],
+            spec_query_len=wl.Q,
+            record_rows=None if wl.record_rows is None else sample.new_row)
+        final_np = None if final is None else final.cpu().numpy()
+        errs[l] = check_commit(wl, l, sample, new, written, final_np)
+        # every slot the commit had no reason to write is bitwise unchanged
+        slots = wl.state_indices.cpu().numpy()
+        targets = set()
+        for b in range(wl.B):
+            s = int(slots[b])
+            n = min(max(int(lens_np[b]), 0), wl.Q)
+            if 0 < s < wl.N and n > 0:
+                f = s if final is None else int(final_np[b])
+                if 0 < f < wl.N:
+                    targets.add(f)
+        keep = torch.tensor([s not in targets for s in range(wl.N)],
+                            device=DEV)
+        assert torch.equal(L.state[keep], before[l][keep])
+    return errs
+
+
+# ---- small workload, in full --------------------------------------------------
+
+@pytest.mark.parametrize("gate", [None, -5.0])
+@pytest.mark.parametrize("dim_first", [True, False])
+def test_tiny_verify_commit(gate, dim_first):
+    wl = make_workload("tiny", DEV, gates=[gate], conv_dim_first=dim_first)
+    sample, ref, errs = _verify_case(wl)
+    cerr = _commit_case(wl, {0: (sample, ref)})
+    print("tiny", gate, dim_first, errs, cerr)
+
+
+# ---- single request and ragged batch, in full ----------------------------------
+
+def test_single_request_full_shape():
+    wl = make_workload("single", DEV)
+    sample, ref, errs = _verify_case(wl)
+    cerr = _commit_case(wl, {0: (sample, ref)})
+    print("single", errs, cerr)
+
+
+def test_ragged_batch_with_null_slots():
+    wl = make_workload("ragged", DEV)
+    assert int((wl.state_indices == 0).sum()) == 6
+    sample, ref, errs = _verify_case(wl)
+    cerr = _commit_case(wl, {0: (sample, ref)})
+    print("ragged", errs, cerr)
+
+
+# ---- sweeps over head dim, window, dtypes, layouts -------------------------------
+
+SWEEP = [(16, 1), (16, 4), (16, 7), (32, 3), (32, 8), (64, 4), (64, 6),
+         (64, 12), (128, 1), (128, 2), (128, 5), (128, 8), (128, 16),
+         (16, 16), (32, 16)]
+
+
+@pytest.mark.parametrize("D,Q", SWEEP)
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_sweep_head_dim_and_window(D, Q, act):
+    wl = make_workload("ragged", DEV, B=7, H=3, D=D, Q=Q, N=12, act=act,
+                       weight=act, null_frac=0.15,
+                       conv_dim_first=(D + Q) % 2 == 0,
+                       gates=[-5.0 if Q % 2 else None], act_row_pad=8)
+    sample, ref, errs = _verify_case(wl)
+    _commit_case(wl, {0: (sample, ref)})
+
+
+@pytest.mark.parametrize("out_dtype,kg_dtype", [("act", "f32"),
+                                                ("f32", "act"),
+                                                ("act", "act")])
+def test_activation_dtype_outputs_and_records(out_dtype, kg_dtype):
+    wl = make_workload("ragged", DEV, B=12, H=4, D=128, Q=4, N=20,
+                       out_dtype=out_dtype, kg_dtype=kg_dtype)
+    # A bf16 key record (the ops page's layout) makes verify and commit see
+    # different key roundings: hold it to one bf16 step.
+    kg_tol = 2 ** -8 if kg_dtype == "act" else None
+    sample, ref, errs = _verify_case(wl, kg_tol=kg_tol)
+    if kg_dtype == "f32":
+        _commit_case(wl, {0: (sample, ref)})
+
+
+def test_bf16_out_is_rne_of_fp32_out():
+    wl = make_workload("ragged", DEV, B=16, H=4, D=128, Q=4, N=24)
+    L = wl.layers[0]
+    page0 = L.page.clone()
+    drive.verify(wl, 0, _counter())
+    out32 = L.out.clone()
+    L.page.copy_(page0)
+    out16 = torch.empty_like(out32, dtype=torch.bfloat16)
+    kw = drive.verify_kwargs(wl, 0, _counter())
+    kw["out"] = out16
+    kda.conv_update_verify(**kw)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out16), bits(out32.to(torch.bfloat16)))
+
+
+# ---- edge cases -----------------------------------------------------------------
+
+def test_edge_cases_verify_and_commit():
+    wl = make_workload("ragged", DEV, B=9, H=2, D=32, Q=4, N=16, act="f32",
+                       weight="f32", null_frac=0.0)
+    qsl = wl.query_start_loc.cpu().numpy()
+    # request 1 has no tokens; request 4 points past the pool; request 6
+    # has a negative slot (padding row)
+    lens = np.diff(qsl)
+    lens[1] = 0
+    qsl = np.concatenate([[0], np.cumsum(lens)])
+    wl.query_start_loc.copy_(torch.tensor(qsl, dtype=torch.int32))
+    T = int(qsl[-1])
+    for L in wl.layers:
+        L.mixed_qkv = L.mixed_qkv[:T]
+        L.raw_gate = L.raw_gate[:T]
+        L.raw_beta = L.raw_beta[:T]
+        L.out = L.out[:T]
+    wl.T = T
+    slots = wl.state_indices.clone()
+    slots[4] = wl.N + 7
+    slots[6] = -1
+    wl.state_indices.copy_(slots)
+    # accepted counts outside [1, Q] are clamped
+    acc = wl.num_accepted_tokens.clone()
+    acc[0], acc[2] = 0, 99
+    wl.num_accepted_tokens.copy_(acc)
+    sample, ref, _ = _verify_case(wl)
+    # commit lengths: 0, over-long (clamped to Q), negative
+    lens_c = wl.commit_lens.clone()
+    lens_c[0], lens_c[2], lens_c[3] = 0, 50, -3
+    _commit_case(wl, {0: (sample, ref)}, lens=lens_c)
+
+
+def test_commit_to_final_slots():
+    wl = make_workload("ragged", DEV, B=6, H=2, D=64, Q=4, N=20,
+                       null_frac=0.0)
+    sample, ref, _ = _verify_case(wl)
+    slots = wl.state_indices.cpu().numpy()
+    free = [s for s in range(1, wl.N) if s not in set(slots.tolist())]
+    final = torch.tensor(free[:wl.B], dtype=torch.int32, device=DEV)
+    final[3] = 0                       # null final slot: skipped
+    src_before = wl.layers[0].state.clone()
+    _commit_case(wl, {0: (sample, ref)}, final=final)
+    # sources are untouched when the result goes to the final slot
+    si = torch.tensor(slots, device=DEV).long()
+    assert torch.equal(wl.layers[0].state[si], src_before[si])
+
+
+def test_record_rows_negative_row_writes_no_records():
+    wl = make_workload("deferred", DEV, B=10, H=2, D=32, Q=4, N=24)
+    rows = wl.record_rows.clone()
+    rows[3] = -1
+    wl.record_rows.copy_(rows)
+    sample, ref, _ = _verify_case(wl)
+    assert sample.new_row[3] == -1
+
+
+# ---- scheduling: determinism, counter protocol, graph replay ----------------------
+
+def test_results_independent_of_grid_size():
+    wl = make_workload("ragged", DEV, B=20, H=8, D=128, Q=4, N=32)
+    L = wl.layers[0]
+    page0, rec0 = L.page.clone(), None
+    outs = []
+    for grid in (1, 3, 0):
+        L.page.copy_(page0)
+        drive.verify(wl, 0, _counter(), max_workgroups=grid)
+        torch.cuda.synchronize()
+        outs.append((L.out.clone(), L.page.clone()))
+    for o, p in outs[1:]:
+        assert torch.equal(bits(o), bits(outs[0][0]))
+        assert torch.equal(p, outs[0][1])
+
+
+def test_counter_protocol_and_reset():
+    wl = make_workload("ragged", DEV, B=8, H=2, D=16, Q=4, N=12)
+    c = _counter()
+    for _ in range(3):
+        drive.verify(wl, 0, c, max_workgroups=5)
+        torch.cuda.synchronize()
+        assert int(c.item()) == 0
+    c.fill_(123)
+    kda.reset_counter(c)
+    torch.cuda.synchronize()
+    assert int(c.item()) == 0
+
+
+def test_verify_graph_replay_matches_eager():
+    wl = make_workload("ragged", DEV, B=16, H=4, D=128, Q=4, N=24)
+    L = wl.layers[0]
+    page0 = L.page.clone()
+    counter = _counter()
+    drive.verify(wl, 0, counter)
+    torch.cuda.synchronize()
+    eager_out, eager_page = L.out.clone(), L.page.clone()
+    L.page.copy_(page0)
+    L.out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            drive.verify(wl, 0, counter)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        L.page.copy_(page0)          # eager work between replays
+        L.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(counter.item()) == 0
+        assert torch.equal(bits(L.out), bits(eager_out))
+        assert torch.equal(L.page, eager_page)
+
+
+# ---- full-size workloads on sampled requests ----------------------------------------
+
+def test_headline_workload_sampled():
+    wl = make_workload("headline", DEV)
+    reqs = list(range(0, wl.B, 8))
+    sample, ref, errs = _verify_case(wl, reqs=reqs)
+    cerr = _commit_case(wl, {0: (sample, ref)})
+    print("headline", errs, cerr)
+
+
+def test_large_multilayer_commit_sampled():
+    wl = make_workload("large", DEV)
+    reqs = list(range(0, wl.B, 16))
+    checked = {0: None, 11: None, 23: None}
+    for layer in range(len(wl.layers)):
+        if layer in checked:
+            sample, ref, errs = _verify_case(wl, layer, reqs=reqs)
+            checked[layer] = (sample, ref)
+        else:
+            drive.verify(wl, layer, _counter())
+    torch.cuda.synchronize()
+    errs = _commit_case(wl, checked)          # one launch, all 24 layers
+    print("large", errs)
+
+
+def test_deferred_sequence_sampled():
+    wl = make_workload("deferred", DEV)
+    reqs = list(range(0, wl.B, 32))
+    # previous step: verify both layers, creating the records
+    first = {}
+    for layer in range(2):
+        first[layer] = snapshot(wl, layer, reqs)
+        drive.verify(wl, layer, _counter())
+    torch.cuda.synchronize()
+    # this step: fold the pending tokens of every layer in one launch,
+    # then verify each layer from the committed checkpoints
+    ctx = drive.commit_context(wl)
+    ctx.commit(wl.state_indices, wl.commit_lens, record_rows=wl.record_rows)
+    torch.cuda.synchronize()
+    pending = wl.commit_lens.cpu().numpy()
+    for layer in range(2):
+        L = wl.layers[layer]
+        s0 = first[layer]
+        r0 = run_oracle_verify(s0)
+        (new, written), = oracle.commit(
+            layers=[commit_layer_inputs(s0, r0, L)],
+            state_indices=s0.new_slot, commit_lens=pending[s0.reqs],
+            spec_query_len=wl.Q, record_rows=s0.new_row)
+        check_commit(wl, layer, s0, new, written)
+        # second verify on the oracle side: committed state, rolled conv
+        # state and the previous step's records as inputs
+        inp = dict(s0.inputs)
+        inp["state"] = new
+        inp["conv_state"] = r0["conv_state"]
+        inp["correction"] = r0["correction"]
+        inp["key_gate"] = r0["key_gate"]
+        s1 = snapshot(wl, layer, reqs)
+        ref1 = oracle.conv_update_verify(**inp)
+        counter = _counter()
+        drive.verify(wl, layer, counter)
+        torch.cuda.synchronize()
+        errs = check_verify(wl, layer, s1, ref1)
+        print("deferred", layer, errs)

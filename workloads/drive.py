@@ -1,0 +1,60 @@
+"""Runs a seeded Workload through the HIP library's Python binding.
+
+Argument plumbing only (which tensor goes to which parameter); used by the
+GPU tests and bench.py.  Not imported by `workloads/__init__` so that the
+oracle tests never load the HIP library.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+import linear_attention_speculative_amd as kda
+
+from .gen import Workload
+
+
+def verify_kwargs(wl: Workload, layer: int, counter: torch.Tensor,
+                  max_workgroups: int = 0) -> dict:
+    L = wl.layers[layer]
+    return dict(
+        mixed_qkv=L.mixed_qkv, raw_gate=L.raw_gate, raw_beta=L.raw_beta,
+        A_log=L.A_log, dt_bias=L.dt_bias,
+        lower_bound=L.lower_bound if L.use_lower_bound else None,
+        state=L.state, correction=L.correction, key_gate=L.key_gate,
+        out=L.out, conv_state=L.conv_state, conv_weight=L.conv_weight,
+        query_start_loc=wl.query_start_loc, state_indices=wl.state_indices,
+        num_accepted_tokens=wl.num_accepted_tokens,
+        spec_query_len=wl.Q, conv_dim_first=wl.conv_dim_first,
+        work_counter=counter, record_rows=wl.record_rows,
+        null_block_id=wl.null_block_id, max_workgroups=max_workgroups)
+
+
+def verify(wl: Workload, layer: int, counter: torch.Tensor,
+           max_workgroups: int = 0, stream=None) -> None:
+    kda.conv_update_verify(stream=stream,
+                           **verify_kwargs(wl, layer, counter,
+                                           max_workgroups))
+
+
+def commit_context(wl: Workload, layers: Optional[list] = None
+                   ) -> kda.CommitContext:
+    idx = range(len(wl.layers)) if layers is None else layers
+    return kda.CommitContext(
+        [dict(state=wl.layers[i].state, correction=wl.layers[i].correction,
+              key_gate=wl.layers[i].key_gate, A_log=wl.layers[i].A_log,
+              dt_bias=wl.layers[i].dt_bias,
+              lower_bound=wl.layers[i].lower_bound
+              if wl.layers[i].use_lower_bound else None) for i in idx],
+        spec_query_len=wl.Q, null_block_id=wl.null_block_id)
+
+
+def commit(wl: Workload, ctx: kda.CommitContext,
+           commit_lens: Optional[torch.Tensor] = None,
+           final_state_indices: Optional[torch.Tensor] = None,
+           stream=None) -> None:
+    ctx.commit(wl.state_indices,
+               wl.commit_lens if commit_lens is None else commit_lens,
+               final_state_indices=final_state_indices,
+               record_rows=wl.record_rows, stream=stream)

@@ -226,6 +226,14 @@ def make_workload(name: str, device="cpu", *, seed: Optional[int] = None,
     page_bytes = conv_bytes + state_bytes + (corr_bytes + kg_bytes
                                              if rec_in_page else 0) + 256
     tdt = _TORCH_DTYPE
+    # Byte ranges the views cover inside a page (the rest is padding).
+    used = {"conv": (0, C * Lc * _ELEM[act]),
+            "state": (conv_bytes, H * D * D * 4)}
+    rec_off = conv_bytes + state_bytes if rec_in_page else 0
+    used["correction"] = (rec_off, H * Q * D * 4)
+    used["key_gate"] = (rec_off + corr_bytes, H * Q * 2 * D * _ELEM[kg_dt])
+    wl.meta["page_views"] = used
+    wl.meta["records_in_page"] = rec_in_page
 
     for layer_idx, lb in enumerate(cfg["gates"]):
         page = torch.randint(0, 256, (N, page_bytes), generator=gen,
