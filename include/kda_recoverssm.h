@@ -125,18 +125,26 @@ typedef struct {
   const int32_t* num_accepted_tokens;  /* [batch] conv history offset + 1 */
   const int32_t* record_rows;          /* [batch] record row, or NULL: the
                                           request's state slot */
-  int32_t* work_counter;   /* device int32[1]: ticket counter.  Must be 0
-                              before the first launch; every launch leaves it
-                              at 0.  One counter per launch in flight. */
+  int32_t* work_counter;   /* device int32[1]: ticket counter of the
+                              persistent schedule (max_workgroups > 0, or a
+                              batch above 65535).  Must be 0 before the first
+                              launch; every launch leaves it at 0.  One
+                              counter per launch in flight.  May be NULL when
+                              the persistent schedule is not used. */
   int32_t batch;
   int32_t spec_query_len;  /* Q */
   int32_t null_block_id;   /* slots <= this are null (0 in vLLM) */
   int32_t conv_dim_first;  /* 1: conv_state is [N, 3HD, Lc]; 0: [N, Lc, 3HD] */
   int32_t use_lower_bound; /* 1: g = lower_bound*sigmoid(A x); 0: softplus */
   float lower_bound;
-  int32_t max_workgroups;  /* persistent grid size; 0 = one full wave of
-                              resident workgroups on the device */
-  int32_t reserved;
+  int32_t max_workgroups;  /* 0: one workgroup per (request, head), handed
+                              out by the hardware dispatcher in request-major
+                              order (the default, and the fastest measured);
+                              > 0: a persistent grid of at most this many
+                              workgroups that draw (request, head) items
+                              from work_counter */
+  int32_t items_per_ticket; /* (request, head) items claimed per ticket;
+                               0 = library default */
 } kda_verify_args;
 
 /* Arguments of kda_recoverssm_commit.  Per-layer tensors are described by
@@ -163,7 +171,9 @@ typedef struct {
   int64_t correction_strides[2];  /* head, position; dim stride is 1 */
   int64_t key_gate_strides[2];    /* head, position; dim stride is 1 */
   int32_t key_gate_dtype;         /* kda_dtype */
-  int32_t reserved0;
+  int32_t max_workgroups;         /* 0: one workgroup per (layer, request,
+                                     head); > 0: a persistent grid of at
+                                     most this many workgroups */
   const float* A_log;             /* device F32 [L, H] */
   int64_t A_log_strides[2];
   const float* dt_bias;           /* device F32 [L, H, D] */

@@ -49,7 +49,7 @@ class KdaVerifyArgs(Structure):
         ("batch", c_int32), ("spec_query_len", c_int32),
         ("null_block_id", c_int32), ("conv_dim_first", c_int32),
         ("use_lower_bound", c_int32), ("lower_bound", c_float),
-        ("max_workgroups", c_int32), ("reserved", c_int32),
+        ("max_workgroups", c_int32), ("items_per_ticket", c_int32),
     ]
 
 
@@ -66,7 +66,7 @@ class KdaCommitArgs(Structure):
         ("key_gate_block_strides", c_void_p),
         ("state_strides", c_int64 * 2), ("correction_strides", c_int64 * 2),
         ("key_gate_strides", c_int64 * 2),
-        ("key_gate_dtype", c_int32), ("reserved0", c_int32),
+        ("key_gate_dtype", c_int32), ("max_workgroups", c_int32),
         ("A_log", c_void_p), ("A_log_strides", c_int64 * 2),
         ("dt_bias", c_void_p), ("dt_bias_strides", c_int64 * 3),
         ("use_lower_bound", c_void_p), ("lower_bound", c_void_p),

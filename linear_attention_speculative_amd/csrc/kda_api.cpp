@@ -258,12 +258,15 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
     return fail(KDA_E_UNALIGNED, "raw_beta is not element aligned");
 
   // Metadata.
+  if (a->items_per_ticket < 0)
+    return fail(KDA_E_ARG, "items_per_ticket is negative");
   if (a->batch > 0) {
     if (!a->query_start_loc || !a->state_indices || !a->num_accepted_tokens)
       return fail(KDA_E_ARG,
                   "query_start_loc, state_indices and num_accepted_tokens "
                   "are required");
-    if (!a->work_counter) return fail(KDA_E_ARG, "work_counter is NULL");
+    if (!a->work_counter && (a->max_workgroups > 0 || a->batch > 65535))
+      return fail(KDA_E_ARG, "the persistent schedule needs a work_counter");
     const void* ptrs[] = {a->query_start_loc, a->state_indices,
                           a->num_accepted_tokens, a->record_rows,
                           a->work_counter};
@@ -273,35 +276,55 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
                                      "aligned");
   }
 
+  // Every stride and every in-item offset the kernel forms must fit in 32
+  // bits (slot and row strides are applied in 64-bit arithmetic).
+  const int64_t i32max = 0x7fffffff;
+  const int64_t strides[] = {
+      a->mixed_qkv.stride[0], a->raw_gate.stride[0], a->raw_beta.stride[0],
+      S.stride[0], a->correction.stride[0], a->correction.stride[1],
+      a->correction.stride[2], a->key_gate.stride[0], a->key_gate.stride[1],
+      a->key_gate.stride[2], a->out.stride[0], cs.stride[0], cs.stride[1],
+      cs.stride[2], a->conv_weight.stride[0], a->conv_weight.stride[1]};
+  for (int64_t st : strides)
+    if (st < 0 || st > i32max)
+      return fail(KDA_E_LAYOUT, "a tensor stride is negative or exceeds 2^31");
+  const int64_t s_chan = a->conv_dim_first ? cs.stride[1] : cs.stride[2];
+  const int64_t s_tok = a->conv_dim_first ? cs.stride[2] : cs.stride[1];
+  if (C3 * s_chan + Lc * s_tok > i32max ||
+      C3 * a->conv_weight.stride[0] > i32max ||
+      Q * (a->mixed_qkv.stride[0] + a->raw_gate.stride[0] +
+           a->raw_beta.stride[0] + a->out.stride[0]) > i32max)
+    return fail(KDA_E_LAYOUT, "per-request offsets exceed 2^31 elements");
+
   kda::VerifyParams& p = plan->p;
   p = kda::VerifyParams{};
   p.mixed_qkv = a->mixed_qkv.data;
-  p.s_x = a->mixed_qkv.stride[0];
+  p.s_x = int32_t(a->mixed_qkv.stride[0]);
   p.raw_gate = a->raw_gate.data;
-  p.s_g = a->raw_gate.stride[0];
+  p.s_g = int32_t(a->raw_gate.stride[0]);
   p.raw_beta = a->raw_beta.data;
-  p.s_beta = a->raw_beta.stride[0];
+  p.s_beta = int32_t(a->raw_beta.stride[0]);
   p.A_log = static_cast<const float*>(a->A_log.data);
   p.dt_bias = static_cast<const float*>(dtb.data);
   p.state = static_cast<const float*>(S.data);
-  p.s_slot = S.stride[0];
+  p.s_slot = int32_t(S.stride[0]);
   p.correction = static_cast<float*>(a->correction.data);
-  p.s_c_row = a->correction.stride[0];
-  p.s_c_head = a->correction.stride[1];
-  p.s_c_pos = a->correction.stride[2];
+  p.s_c_row = int32_t(a->correction.stride[0]);
+  p.s_c_head = int32_t(a->correction.stride[1]);
+  p.s_c_pos = int32_t(a->correction.stride[2]);
   p.key_gate = a->key_gate.data;
-  p.s_kg_row = a->key_gate.stride[0];
-  p.s_kg_head = a->key_gate.stride[1];
-  p.s_kg_pos = a->key_gate.stride[2];
+  p.s_kg_row = int32_t(a->key_gate.stride[0]);
+  p.s_kg_head = int32_t(a->key_gate.stride[1]);
+  p.s_kg_pos = int32_t(a->key_gate.stride[2]);
   p.out = a->out.data;
-  p.s_out = a->out.stride[0];
+  p.s_out = int32_t(a->out.stride[0]);
   p.conv_state = cs.data;
-  p.s_cs_slot = cs.stride[0];
-  p.s_cs_chan = a->conv_dim_first ? cs.stride[1] : cs.stride[2];
-  p.s_cs_tok = a->conv_dim_first ? cs.stride[2] : cs.stride[1];
+  p.s_cs_slot = int32_t(cs.stride[0]);
+  p.s_cs_chan = int32_t(s_chan);
+  p.s_cs_tok = int32_t(s_tok);
   p.conv_weight = a->conv_weight.data;
-  p.s_w_chan = a->conv_weight.stride[0];
-  p.s_w_tap = a->conv_weight.stride[1];
+  p.s_w_chan = int32_t(a->conv_weight.stride[0]);
+  p.s_w_tap = int32_t(a->conv_weight.stride[1]);
   p.qsl = a->query_start_loc;
   p.slots = a->state_indices;
   p.accepted = a->num_accepted_tokens;
@@ -310,16 +333,17 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
   p.B = a->batch;
   p.H = int32_t(H);
   p.Q = int32_t(Q);
-  p.N = N > 0x7fffffff ? 0x7fffffff : int32_t(N);
-  p.R = R > 0x7fffffff ? 0x7fffffff : int32_t(R);
+  p.N = N > i32max ? int32_t(i32max) : int32_t(N);
+  p.R = R > i32max ? int32_t(i32max) : int32_t(R);
   p.T = int32_t(T);
   p.null_id = a->null_block_id;
-  p.out_bf16 = a->out.dtype == KDA_BF16;
-  p.kg_bf16 = a->key_gate.dtype == KDA_BF16;
-  p.w_bf16 = a->conv_weight.dtype == KDA_BF16;
-  p.use_lb = a->use_lower_bound != 0;
+  p.flags = (a->out.dtype == KDA_BF16 ? kda::kOutBf16 : 0) |
+            (a->key_gate.dtype == KDA_BF16 ? kda::kKgBf16 : 0) |
+            (a->conv_weight.dtype == KDA_BF16 ? kda::kWBf16 : 0) |
+            (a->use_lower_bound ? kda::kLowerBound : 0);
   p.lb = a->lower_bound;
   p.n_items = int32_t(int64_t(a->batch) * H);
+  p.per_ticket = a->items_per_ticket;
   plan->D = int(D);
   plan->act_bf16 = act == KDA_BF16;
   plan->noop = a->batch == 0 || T == 0;
@@ -425,6 +449,7 @@ int plan_commit(const kda_commit_args* a, CommitPlan* plan) {
   p.N = a->num_slots;
   p.R = a->num_record_rows;
   p.kg_bf16 = a->key_gate_dtype == KDA_BF16;
+  p.grid = a->max_workgroups;
   plan->D = int(D);
   plan->noop = a->batch == 0;
   return KDA_OK;

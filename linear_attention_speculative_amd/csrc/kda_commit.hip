@@ -11,10 +11,13 @@
 // The per-column vectors (Gam, k_hat_t * Suf_t) are built once per head in
 // LDS; each state element then costs 1 + n multiply-adds, so the kernel is a
 // streaming read-modify-write of the 64 KiB tile: 16-byte non-temporal
-// loads issued before the record work, stores to the final slot.
+// loads issued after the small record loads, stores to the final slot.
 //
-// One workgroup per (layer, request, head); blockIdx.x enumerates heads
-// fastest, so consecutive workgroups stream consecutive heads of one slot.
+// Schedules: by default one workgroup per (head, request, layer) on a 3-D
+// grid (heads fastest, so consecutive workgroups stream consecutive heads of
+// one slot); with grid > 0, a persistent grid of that many workgroups walks
+// the items with a stride (fewer streams in flight at once, which the
+// read-modify-write traffic of the HBM can prefer).
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -29,6 +32,7 @@ struct CommitCfg {
   static constexpr int PASSES = D / RPP;
   static constexpr int CW = (D + 63) / 64;  // waves holding columns
   static constexpr int CS = QMAX + 4;       // padded row of corrections
+  static constexpr int JC = (QMAX * D + NT - 1) / NT;  // corrections/thread
   static_assert(RPP * PASSES == D, "tile rows");
 };
 
@@ -41,40 +45,27 @@ struct alignas(16) CommitSmem {
   float red[C::CW][QMAX];  // wave partial sums of |k_t|^2
 };
 
+// Commit of one (layer, request, head).  Returns whether it used LDS (a
+// skipped item returns before touching it).
 template <int D, int QMAX>
-__global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
-    kda_commit_kernel(CommitParams p) {
+__device__ __forceinline__ bool commit_item(const CommitParams& p,
+                                            CommitSmem<D, QMAX>& sm, int l,
+                                            int b, int h) {
   using C = CommitCfg<D, QMAX>;
-  __shared__ CommitSmem<D, QMAX> sm;
   const int tid = threadIdx.x;
-  const int item = blockIdx.x;
-  const int per_layer = p.B * p.H;
-  const int l = uniform(item / per_layer);
-  const int rem = item - l * per_layer;
-  const int b = uniform(rem / p.H);
-  const int h = uniform(rem - b * p.H);
-
   const int slot = p.slots[b];
-  if (slot <= p.null_id || slot < 0 || slot >= p.N) return;
+  if (slot <= p.null_id || slot < 0 || slot >= p.N) return false;
   const int n = min(max(p.commit_lens[b], 0), p.Q);
-  if (n == 0) return;
+  if (n == 0) return false;
   const int f = p.final_slots ? p.final_slots[b] : slot;
-  if (f <= p.null_id || f < 0 || f >= p.N) return;
+  if (f <= p.null_id || f < 0 || f >= p.N) return false;
   const int r = p.record_rows ? p.record_rows[b] : slot;
-  if (r < 0 || r >= p.R) return;
+  if (r < 0 || r >= p.R) return false;
 
   float* state = reinterpret_cast<float*>(p.state_base[l]);
   const int64_t sbs = p.state_bs[l];
   const float* src = state + int64_t(slot) * sbs + int64_t(h) * p.s_state_head;
   float* dst = state + int64_t(f) * sbs + int64_t(h) * p.s_state_head;
-
-  // Prefetch the whole tile: lane group rg owns rows rg, rg+RPP, ...
-  const int lg = tid % C::L, rg = tid / C::L;
-  const int col = 4 * lg;
-  f4 st[C::PASSES];
-#pragma unroll
-  for (int pp = 0; pp < C::PASSES; ++pp)
-    st[pp] = ld_stream(src + (pp * C::RPP + rg) * D + col);
 
   // Records of this head.
   const float* corr = reinterpret_cast<const float*>(p.corr_base[l]) +
@@ -83,14 +74,21 @@ __global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
   const void* kg = reinterpret_cast<const void*>(p.kg_base[l]);
   const bool kg_bf16 = p.kg_bf16 != 0;
 
-  // Corrections, transposed so that a row's values are contiguous.
-  for (int j = tid; j < QMAX * D; j += C::NT) {
+  // Small loads first (vector-memory counters retire in issue order): the
+  // corrections (transposed so that a row's values are contiguous), the raw
+  // keys and gates, the gate parameters; then the state tile.
+  float cv[C::JC];
+#pragma unroll
+  for (int jj = 0; jj < C::JC; ++jj) {
+    const int j = tid + jj * C::NT;
     const int t = j / D, v = j - t * D;
-    sm.cT[v * C::CS + t] = t < n ? corr[int64_t(t) * p.s_c_pos + v] : 0.0f;
+    cv[jj] = (j < QMAX * D && t < n) ? corr[int64_t(t) * p.s_c_pos + v]
+                                     : 0.0f;
   }
 
   // Per column k: raw keys and decays of the committed positions.
-  const float Ah = __expf(p.A_log[int64_t(l) * p.s_A_l + int64_t(h) * p.s_A_h]);
+  const float Ah =
+      __expf(p.A_log[int64_t(l) * p.s_A_l + int64_t(h) * p.s_A_h]);
   const bool use_lb = p.use_lb[l] != 0;
   const float lb = p.lb[l];
   const bool col_ok = tid < D;
@@ -98,18 +96,37 @@ __global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
       col_ok ? p.dt_bias[int64_t(l) * p.s_dt_l + int64_t(h) * p.s_dt_h +
                          int64_t(tid) * p.s_dt_d]
              : 0.0f;
-  float kr[QMAX], dd[QMAX];
+  float kr[QMAX], gr[QMAX], dd[QMAX];
 #pragma unroll
   for (int t = 0; t < QMAX; ++t) {
     kr[t] = 0.0f;
-    dd[t] = 1.0f;
+    gr[t] = 0.0f;
     if (col_ok && t < n) {
       const int64_t o = kg_off + int64_t(t) * p.s_kg_pos;
       kr[t] = ld_elem(kg, o + tid, kg_bf16);
-      const float x = ld_elem(kg, o + D + tid, kg_bf16) + bias;
-      dd[t] = __expf(kda_gate(x, Ah, use_lb, lb));
+      gr[t] = ld_elem(kg, o + D + tid, kg_bf16);
     }
   }
+
+  // The state tile: lane group rg owns rows rg, rg+RPP, ...
+  const int lg = tid % C::L, rg = tid / C::L;
+  const int col = 4 * lg;
+  f4 st[C::PASSES];
+#pragma unroll
+  for (int pp = 0; pp < C::PASSES; ++pp)
+    st[pp] = ld_stream(src + (pp * C::RPP + rg) * D + col);
+
+#pragma unroll
+  for (int jj = 0; jj < C::JC; ++jj) {
+    const int j = tid + jj * C::NT;
+    const int t = j / D, v = j - t * D;
+    if (j < QMAX * D) sm.cT[v * C::CS + t] = cv[jj];
+  }
+#pragma unroll
+  for (int t = 0; t < QMAX; ++t)
+    dd[t] = (col_ok && t < n)
+                ? __expf(kda_gate(gr[t] + bias, Ah, use_lb, lb))
+                : 1.0f;
   const int wave = tid / 64, lane = tid % 64;
   if (wave < C::CW) {
 #pragma unroll
@@ -156,6 +173,34 @@ __global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
     }
     st_stream(dst + row * D + col, acc);
   }
+  return true;
+}
+
+// One workgroup per item: blockIdx = (head, request, layer).
+template <int D, int QMAX>
+__global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
+    kda_commit_grid_kernel(CommitParams p) {
+  __shared__ CommitSmem<D, QMAX> sm;
+  commit_item<D, QMAX>(p, sm, int(blockIdx.z), int(blockIdx.y),
+                       int(blockIdx.x));
+}
+
+// Persistent grid: workgroup g takes items g, g + gridDim.x, ... in
+// (layer, request, head) order, heads fastest.
+template <int D, int QMAX>
+__global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
+    kda_commit_strided_kernel(CommitParams p) {
+  __shared__ CommitSmem<D, QMAX> sm;
+  const int per_layer = p.B * p.H;
+  const int n_items = p.L * per_layer;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int l = uniform(item / per_layer);
+    const int rem = item - l * per_layer;
+    const int b = uniform(rem / p.H);
+    const int h = uniform(rem - b * p.H);
+    // LDS is reused by the next item: wait until every thread is done.
+    if (commit_item<D, QMAX>(p, sm, l, b, h)) lds_barrier();
+  }
 }
 
 template <int D, int QMAX>
@@ -163,8 +208,15 @@ int launch_cq(const CommitParams& p, hipStream_t stream) {
   using C = CommitCfg<D, QMAX>;
   const int64_t items = int64_t(p.L) * p.B * p.H;
   if (items > 0x7fffffff) return int(hipErrorInvalidValue);
-  hipLaunchKernelGGL((kda_commit_kernel<D, QMAX>), dim3(unsigned(items)),
-                     dim3(C::NT), 0, stream, p);
+  if (p.grid <= 0 && p.B <= 65535 && p.L <= 65535) {
+    hipLaunchKernelGGL((kda_commit_grid_kernel<D, QMAX>),
+                       dim3(p.H, p.B, p.L), dim3(C::NT), 0, stream, p);
+  } else {
+    const int64_t g = p.grid > 0 ? p.grid : 4096;
+    hipLaunchKernelGGL((kda_commit_strided_kernel<D, QMAX>),
+                       dim3(unsigned(g < items ? g : items)), dim3(C::NT), 0,
+                       stream, p);
+  }
   return int(hipGetLastError());
 }
 

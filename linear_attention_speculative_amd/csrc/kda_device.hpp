@@ -100,6 +100,48 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Value of the partner lane at distance S inside a 16-lane row, for the
+// pairings used by transpose_sum (each pairs lanes that differ in bit S).
+template <int S>
+__device__ __forceinline__ float partner(float v) {
+  static_assert(S == 1 || S == 2 || S == 4 || S == 8, "stride");
+  if constexpr (S == 8) return dpp<kRowMirror>(v);
+  if constexpr (S == 4) return dpp<kRowHalfMirror>(v);
+  if constexpr (S == 2) return dpp<kQuadXor2>(v);
+  return dpp<kQuadXor1>(v);
+}
+
+// Transposing reduction over aligned groups of G lanes (G <= 16): every lane
+// holds N partial values (N <= G, powers of two); afterwards lane j of a
+// group holds the group total of value index j >> (log2 G - log2 N).  Each
+// halving step keeps one half of the values and adds the partner's copy of
+// that half, so N values cost N - 1 adds instead of N log2 G.
+template <int S, int NLIVE, int N>
+__device__ __forceinline__ void transpose_step(float (&v)[N], int j) {
+  if constexpr (S >= 1) {
+    if constexpr (NLIVE > 1) {
+      const bool upper = (j & S) != 0;
+#pragma unroll
+      for (int k = 0; k < NLIVE / 2; ++k) {
+        const float keep = upper ? v[k + NLIVE / 2] : v[k];
+        const float send = upper ? v[k] : v[k + NLIVE / 2];
+        v[k] = keep + partner<S>(send);
+      }
+      transpose_step<S / 2, NLIVE / 2>(v, j);
+    } else {
+      v[0] += partner<S>(v[0]);
+      transpose_step<S / 2, 1>(v, j);
+    }
+  }
+}
+
+template <int G, int N>
+__device__ __forceinline__ float transpose_sum(float (&v)[N], int j) {
+  static_assert(G >= 1 && G <= 16 && N >= 1 && N <= G, "sizes");
+  transpose_step<G / 2, N>(v, j);
+  return v[0];
+}
+
 // Sum over the whole 64-lane wave, returned as a wave-uniform value.
 __device__ __forceinline__ float wave_sum(float v) {
   v = group_sum<16>(v);
@@ -116,17 +158,23 @@ __device__ __forceinline__ int uniform(int x) {
 
 // ---- KDA math -------------------------------------------------------------------
 
+// Hardware reciprocal (v_rcp_f32, about 1 ulp).
+__device__ __forceinline__ float rcp_(float x) {
+  return __builtin_amdgcn_rcpf(x);
+}
+
 __device__ __forceinline__ float sigmoidf_(float x) {
-  return 1.0f / (1.0f + __expf(-x));
+  return rcp_(1.0f + __expf(-x));
 }
 
 // Log-decay of one channel from x = raw gate + dt_bias and A = exp(A_log):
 // bounded form lb * sigmoid(A x), else -A * softplus(x) where softplus is the
-// identity above 20 (ops page, `_kda_gate`).
+// identity above 20 (ops page, `_kda_gate`).  ln(1 + e^x) loses its low bits
+// for very negative x, where it is below 1e-7 and the decay rounds to 1.
 __device__ __forceinline__ float kda_gate(float x, float A, bool use_lb,
                                           float lb) {
   if (use_lb) return lb * sigmoidf_(A * x);
-  const float sp = x > 20.0f ? x : log1pf(__expf(x));
+  const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
   return -A * sp;
 }
 

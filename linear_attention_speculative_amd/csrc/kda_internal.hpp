@@ -10,30 +10,44 @@ namespace kda {
 constexpr int kConvWidth = 4;   // taps of the short convolution
 constexpr int kMaxWindow = 16;  // largest draft window Q supported
 
-// Everything the verify kernel needs, with strides in elements.
+// Everything the verify kernel needs.  Strides are in elements and fit in
+// 32 bits (checked on the host); keeping them narrow keeps the kernel's
+// wave-uniform state inside the scalar register file.
 struct VerifyParams {
-  const void* mixed_qkv;  int64_t s_x;      // [T, 3HD] row stride
-  const void* raw_gate;   int64_t s_g;      // [T, HD]
-  const void* raw_beta;   int64_t s_beta;   // [T, H]
-  const float* A_log;                        // [H]
-  const float* dt_bias;                      // [H, D]
-  const float* state;     int64_t s_slot;   // [N, H, D, D]
-  float* correction;      int64_t s_c_row, s_c_head, s_c_pos;
-  void* key_gate;         int64_t s_kg_row, s_kg_head, s_kg_pos;
-  void* out;              int64_t s_out;
-  void* conv_state;       int64_t s_cs_slot, s_cs_chan, s_cs_tok;
-  const void* conv_weight; int64_t s_w_chan, s_w_tap;
+  const void* mixed_qkv;    // [T, 3HD]
+  const void* raw_gate;     // [T, HD]
+  const void* raw_beta;     // [T, H]
+  const float* A_log;       // [H]
+  const float* dt_bias;     // [H, D]
+  const float* state;       // [N, H, D, D]
+  float* correction;        // [R, H, Q, D]
+  void* key_gate;           // [R, H, Q, 2D]
+  void* out;                // [T, HD]
+  void* conv_state;         // [N, 3HD, Lc] / [N, Lc, 3HD]
+  const void* conv_weight;  // [3HD, W]
   const int32_t* qsl;
   const int32_t* slots;
   const int32_t* accepted;
-  const int32_t* record_rows;               // may be null
+  const int32_t* record_rows;  // may be null
   int32_t* counter;
+  int32_t s_x, s_g, s_beta, s_slot;
+  int32_t s_c_row, s_c_head, s_c_pos;
+  int32_t s_kg_row, s_kg_head, s_kg_pos;
+  int32_t s_out;
+  int32_t s_cs_slot, s_cs_chan, s_cs_tok;
+  int32_t s_w_chan, s_w_tap;
   int32_t B, H, Q, N, R, T, null_id;
-  int32_t out_bf16, kg_bf16, w_bf16;
-  int32_t use_lb;
+  int32_t flags;            // kOutBf16 | kKgBf16 | kWBf16 | kLowerBound
   float lb;
   int32_t n_items;
+  int32_t per_ticket;       // items claimed per ticket
+  int32_t n_tickets;        // ceil(n_items / per_ticket)
 };
+
+constexpr int32_t kOutBf16 = 1;
+constexpr int32_t kKgBf16 = 2;
+constexpr int32_t kWBf16 = 4;
+constexpr int32_t kLowerBound = 8;
 
 struct CommitParams {
   const int64_t* state_base;  const int64_t* state_bs;
@@ -53,6 +67,7 @@ struct CommitParams {
   int32_t L, B, H, Q, null_id;
   int64_t N, R;
   int32_t kg_bf16;
+  int32_t grid;   // <= 0: one workgroup per item; > 0: persistent, strided
 };
 
 // Launchers (return a hipError_t as int).  `grid` <= 0 means the default.

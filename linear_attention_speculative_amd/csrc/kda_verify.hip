@@ -1,6 +1,7 @@
 // Fused short-conv update + RecoverSSM speculative verify of one KDA layer,
-// for gfx950 (wave64).  One workgroup handles one (request, head) work item
-// at a time and draws items from a ticket counter (persistent grid).
+// for gfx950 (wave64).  One workgroup handles one (request, head) work item:
+// by default one workgroup per item (hardware dispatch); optionally a
+// persistent grid whose workgroups draw items from a ticket counter.
 //
 // What is computed (ops page `_kda_recoverssm_verify_kernel` with the conv
 // update of the kernels page's `CuteRecoverSSMVerify`): for draft positions
@@ -18,17 +19,27 @@
 // only per-head K-vector quantities.  That halves the per-element work of
 // the step-by-step form and keeps the state tile out of the critical path.
 //
+// The kernel is bound by instruction issue long before HBM unless every
+// per-item overhead is small, so: addresses are 32-bit offsets from
+// wave-uniform 64-bit bases; sigmoid/softplus use the hardware exp, log and
+// reciprocal; the K-dimension reductions go through an LDS tree instead of
+// one cross-lane reduction per scalar; the row dot products are reduced with
+// a transposing DPP reduction that leaves one finished value per lane.
+//
 // Phases of one item (LDS barriers between them):
-//   0  issue the 16-byte streaming loads of the state tile into registers;
-//      conv update of the head's 3D channels (history at offset a-1 of the
-//      conv state, SiLU), roll the conv state in place, key record; gate
-//      decays and the raw-gate half of the key record; sigmoid(beta).
+//   0  issue the small loads (conv history, new inputs, taps, gate, beta),
+//      then the 16-byte streaming loads of the state tile into registers
+//      (vector-memory counters retire in issue order, so the small loads go
+//      first and the prologue computes while the tile streams in); conv
+//      update of the head's 3D channels (history at offset a-1 of the conv
+//      state, SiLU), roll the conv state in place, key record; gate decays
+//      and the raw-gate half of the key record; sigmoid(beta).
 //   1  per column k: partial sums of |k_t|^2, |q_t|^2 and of the pairwise
-//      terms <k_s, P_{s,t} k_t>, <k_s, P_{s,t} q_t>; wave reductions.
+//      terms <k_s, P_{s,t} k_t>, <k_s, P_{s,t} q_t>, summed over k in LDS.
 //   2  norms -> per-column vectors Gam_t k_hat_t, Gam_t q_hat_t (LDS) and the
 //      Q x Q coefficient matrices.
-//   3  dot products of every state row with the 2Q vectors; group sums over
-//      the lanes that share a row (DPP); row results to LDS.
+//   3  dot products of every state row with the 2Q vectors; transposing
+//      reduction over the lanes that share a row; row results to LDS.
 //   4  one thread per row: triangular solve for c_t, outputs o_t; stores of
 //      out and of the correction record (coalesced along V).
 #include "kda_device.hpp"
@@ -41,18 +52,31 @@ template <int D, int QMAX>
 struct VerifyCfg {
   static constexpr int NT = D >= 128 ? 256 : (D == 64 ? 128 : 64);
   // lanes sharing one state row in the dot-product phase
-  static constexpr int L =
-      D == 128 ? (QMAX <= 8 ? 16 : 32) : (D == 64 ? 16 : (D == 32 ? 8 : 4));
+  static constexpr int L = D >= 64 ? 16 : (D == 32 ? 8 : 4);
   static constexpr int RPP = NT / L;           // rows per pass
   static constexpr int PASSES = D / RPP;       // passes over the tile
   static constexpr int CHUNKS = D / (4 * L);   // float4 per lane per row
-  static constexpr int CW = (D + 63) / 64;     // waves holding columns
+  static constexpr int NVAL = 2 * PASSES;      // row sums per lane, per t
+  // Column phase: D >= 64 gives NG groups of D threads (whole waves), each
+  // computing a share of the partial sums; below 64 one group does all.
+  static constexpr int NG = D >= 64 ? NT / D : 1;
   static constexpr int NM = QMAX * (QMAX - 1) / 2;  // <k_s, P k_t>, s < t
   static constexpr int NN = QMAX * (QMAX + 1) / 2;  // <k_s, P q_t>, s <= t
   static constexpr int NV = 2 * QMAX + NM + NN;     // reduced scalars
   static constexpr int DS = 2 * QMAX + 4;           // padded row of dots
+  // LDS reduction tree: columns are summed in chunks of CH, NB scalars at
+  // a time (the whole set when it fits in 48 KiB).
+  static constexpr int CH = D >= 32 ? 32 : D;
+  static constexpr int NCH = D / CH;
+  static constexpr int NB = NV * D <= 12288 ? NV : 12288 / D;
+  static constexpr int PART = NB * D > D * DS ? NB * D : D * DS;
+  static constexpr int JC = (3 * D + NT - 1) / NT;  // conv channels/thread
+  static constexpr int JG = (QMAX * D + NT - 1) / NT;  // gate values/thread
+  // Keep the register budget for 4 waves per SIMD.
+  static constexpr int MIN_WAVES = 4;
   static_assert(RPP * PASSES == D, "tile rows");
   static_assert(CHUNKS * 4 * L == D, "tile columns");
+  static_assert(NVAL <= L, "one row sum per lane");
 };
 
 template <int D, int QMAX>
@@ -61,8 +85,10 @@ struct alignas(16) VerifySmem {
   float y[3][QMAX][D];           // conv outputs q | k | v, positions < q
   float dec[QMAX][D];            // decays d_t
   float vec[2 * QMAX][D];        // Gam_t k_hat_t, then Gam_t q_hat_t
-  float dots[D * C::DS];         // per row: S.(Gam k_hat_t), S.(Gam q_hat_t)
-  float red[C::CW][C::NV];       // wave partial sums
+  // column partial sums [NB][D] (phase 1), then per row:
+  // S.(Gam k_hat_t), S.(Gam q_hat_t) [D][DS] (phases 3-4)
+  float part[C::PART];
+  float red[C::NV * C::NCH];     // chunk sums of the column partials
   float Mc[QMAX][QMAX];          // <k_hat_s, P_{s,t} k_hat_t>, s < t
   float Nc[QMAX][QMAX];          // <k_hat_s, P_{s,t} q_hat_t>, s <= t
   float beta[QMAX];
@@ -79,140 +105,226 @@ __device__ __forceinline__ constexpr int idx_n(int t, int s) {
   return 2 * QMAX + QMAX * (QMAX - 1) / 2 + t * (t + 1) / 2 + s;
 }
 
-template <int D, int QMAX, bool ACT_BF16>
+// Wave-uniform description of one (request, head) work item.
+struct Item {
+  int b, h, bos, q, slot, r, a;
+  bool live, rec_ok;
+};
+
+__device__ __forceinline__ Item load_item(const VerifyParams& p, int b,
+                                          int h) {
+  Item it;
+  it.b = b;
+  it.h = h;
+  // Token rows outside [0, T) are never touched (memory-safety clamp).
+  it.bos = p.qsl[it.b];
+  const int eos = p.qsl[it.b + 1];
+  it.q = (it.bos < 0 || it.bos >= p.T)
+             ? 0
+             : min(min(max(eos - it.bos, 0), p.Q), p.T - it.bos);
+  it.slot = p.slots[it.b];
+  it.live = it.q > 0 && it.slot > p.null_id && it.slot >= 0 &&
+            it.slot < p.N;
+  it.a = min(max(p.accepted[it.b], 1), p.Q);
+  it.r = p.record_rows ? p.record_rows[it.b] : it.slot;
+  it.rec_ok = it.r >= 0 && it.r < p.R;
+  return it;
+}
+
+// One live item.  `drawn` is thread 0's freshly drawn ticket (meaningful
+// on the last item of a chunk); it is published through LDS at the first
+// barrier, after which `advance()` lets every thread start the scalar loads
+// of the next item's metadata early.
+// FULL: the request verifies all QMAX positions (q == QMAX), so every
+// position guard folds away at compile time.
+template <int D, int QMAX, bool ACT_BF16, bool FULL, class Advance>
 __device__ __forceinline__ void verify_item(const VerifyParams& p,
-                                            VerifySmem<D, QMAX>& sm, int b,
-                                            int h) {
+                                            VerifySmem<D, QMAX>& sm,
+                                            const Item& it, int drawn,
+                                            int buf, Advance&& advance) {
   using C = VerifyCfg<D, QMAX>;
   using A = Act<ACT_BF16>;
   using AT = typename A::T;
   const int tid = threadIdx.x;
+  const int h = it.h;
+  const int q = FULL ? QMAX : it.q;
+  const bool rec_ok = it.rec_ok;
+  const int HD = p.H * D;
 
-  // Token rows outside [0, T) are never touched (memory-safety clamp).
-  const int bos = p.qsl[b];
-  const int q = (bos < 0 || bos >= p.T)
-                    ? 0
-                    : min(min(max(p.qsl[b + 1] - bos, 0), p.Q), p.T - bos);
-  const int slot = p.slots[b];
-  if (q == 0) return;
-  const int64_t out_col = int64_t(h) * D;
-  if (slot <= p.null_id || slot < 0 || slot >= p.N) {
-    // Null block: zero outputs, touch no state, record or conv byte.
-    for (int j = tid; j < q * D; j += C::NT) {
-      const int t = j / D, v = j - t * D;
-      st_elem(p.out, int64_t(bos + t) * p.s_out + out_col + v, 0.0f,
-              p.out_bf16);
+  // Wave-uniform 64-bit bases of everything this item touches; lanes add
+  // 32-bit offsets (the host checks that in-item offsets fit).
+  const AT* __restrict__ xq =
+      static_cast<const AT*>(p.mixed_qkv) + int64_t(it.bos) * p.s_x;
+  AT* __restrict__ cs =
+      static_cast<AT*>(p.conv_state) + int64_t(it.slot) * p.s_cs_slot;
+  const AT* __restrict__ graw = static_cast<const AT*>(p.raw_gate) +
+                                int64_t(it.bos) * p.s_g + h * D;
+  const AT* __restrict__ rbeta = static_cast<const AT*>(p.raw_beta) +
+                                 int64_t(it.bos) * p.s_beta + h;
+  const int64_t kg_off =
+      int64_t(it.r) * p.s_kg_row + int64_t(h) * p.s_kg_head;
+  float* __restrict__ kg32 = static_cast<float*>(p.key_gate) + kg_off;
+  uint16_t* __restrict__ kg16 = static_cast<uint16_t*>(p.key_gate) + kg_off;
+  const int s_x = p.s_x, s_g = p.s_g, s_beta = p.s_beta;
+  const int s_cc = p.s_cs_chan, s_ct = p.s_cs_tok;
+  const int s_kp = p.s_kg_pos;
+  const bool kg_bf16 = (p.flags & kKgBf16) != 0;
+
+  // ---- phase 0a: small loads first -------------------------------------------
+  AT hist[C::JC][3];
+  AT xs[C::JC][QMAX];
+  float w[C::JC][4];
+#pragma unroll
+  for (int jj = 0; jj < C::JC; ++jj) {
+    const int j = tid + jj * C::NT;
+    if (j < 3 * D) {
+      const int part = j / D, d = j - part * D;
+      const int ch = part * HD + h * D + d;
+      const int co = ch * s_cc + (it.a - 1) * s_ct;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) hist[jj][i] = cs[co + i * s_ct];
+      const int wo = ch * p.s_w_chan;
+      const int wt = p.s_w_tap;
+      if (p.flags & kWBf16) {
+        const uint16_t* wp = static_cast<const uint16_t*>(p.conv_weight) + wo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[jj][i] = bf16_to_f32(wp[i * wt]);
+      } else {
+        const float* wp = static_cast<const float*>(p.conv_weight) + wo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[jj][i] = wp[i * wt];
+      }
+#pragma unroll
+      for (int t = 0; t < QMAX; ++t)
+        if (t < q) xs[jj][t] = xq[t * s_x + ch];
     }
-    return;
   }
-  const int r = p.record_rows ? p.record_rows[b] : slot;
-  const bool rec_ok = r >= 0 && r < p.R;
-  const int a = min(max(p.accepted[b], 1), p.Q);
+  AT gv[C::JG];
+  float gb[C::JG];
+#pragma unroll
+  for (int jj = 0; jj < C::JG; ++jj) {
+    const int j = tid + jj * C::NT;
+    const int t = j / D, k = j - t * D;
+    if (t < q) {
+      gv[jj] = graw[t * s_g + k];
+      gb[jj] = p.dt_bias[h * D + k];
+    }
+  }
+  AT bv{};
+  if (tid < q) bv = rbeta[tid * s_beta];
+  const float Ah = __expf(p.A_log[h]);
 
-  // ---- phase 0: prefetch the state tile (rows across lane groups) --------
+  // ---- phase 0b: first half of the state tile into registers -------------
+  // (the second half is issued once the conv registers are free)
   const int lg = tid % C::L;      // lane within its row group
   const int rg = tid / C::L;      // row group
-  const float* sbase =
-      p.state + int64_t(slot) * p.s_slot + int64_t(h) * D * D;
+  const float* __restrict__ sbase =
+      p.state + int64_t(it.slot) * p.s_slot + int64_t(h) * D * D;
+  constexpr int P0 = (C::PASSES + 1) / 2;
   f4 st[C::PASSES][C::CHUNKS];
 #pragma unroll
-  for (int pp = 0; pp < C::PASSES; ++pp)
+  for (int pp = 0; pp < P0; ++pp)
 #pragma unroll
     for (int c = 0; c < C::CHUNKS; ++c)
       st[pp][c] = ld_stream(sbase + (pp * C::RPP + rg) * D + c * 4 * C::L +
                             4 * lg);
 
-  // ---- phase 0: conv update, roll, key record ------------------------------
-  const AT* xq = static_cast<const AT*>(p.mixed_qkv) + int64_t(bos) * p.s_x;
-  AT* cs = static_cast<AT*>(p.conv_state) + int64_t(slot) * p.s_cs_slot;
-  const int64_t kg_base =
-      int64_t(r) * p.s_kg_row + int64_t(h) * p.s_kg_head;
-  for (int j = tid; j < 3 * D; j += C::NT) {
-    const int part = j / D, d = j - part * D;
-    const int64_t ch = int64_t(part) * p.H * D + int64_t(h) * D + d;
-    AT* csc = cs + ch * p.s_cs_chan;
-    const AT h0 = csc[int64_t(a - 1) * p.s_cs_tok];
-    const AT h1 = csc[int64_t(a) * p.s_cs_tok];
-    const AT h2 = csc[int64_t(a + 1) * p.s_cs_tok];
-    const float w0 = ld_elem(p.conv_weight, ch * p.s_w_chan, p.w_bf16);
-    const float w1 = ld_elem(p.conv_weight, ch * p.s_w_chan + p.s_w_tap,
-                             p.w_bf16);
-    const float w2 = ld_elem(p.conv_weight, ch * p.s_w_chan + 2 * p.s_w_tap,
-                             p.w_bf16);
-    const float w3 = ld_elem(p.conv_weight, ch * p.s_w_chan + 3 * p.s_w_tap,
-                             p.w_bf16);
-    AT xs[QMAX];
+  // ---- phase 0c: conv + SiLU, key record, roll ------------------------------
 #pragma unroll
-    for (int t = 0; t < QMAX; ++t)
-      if (t < q) xs[t] = xq[int64_t(t) * p.s_x + ch];
-    float s0 = A::f(h0), s1 = A::f(h1), s2 = A::f(h2);
+  for (int jj = 0; jj < C::JC; ++jj) {
+    const int j = tid + jj * C::NT;
+    if (j < 3 * D) {
+      const int part = j / D, d = j - part * D;
+      const int ch = part * HD + h * D + d;
+      float s0 = A::f(hist[jj][0]), s1 = A::f(hist[jj][1]),
+            s2 = A::f(hist[jj][2]);
 #pragma unroll
-    for (int t = 0; t < QMAX; ++t) {
-      if (t < q) {
-        const float s3 = A::f(xs[t]);
-        float acc = w0 * s0;
-        acc = fmaf(w1, s1, acc);
-        acc = fmaf(w2, s2, acc);
-        acc = fmaf(w3, s3, acc);
-        const float yv = acc * sigmoidf_(acc);
-        sm.y[part][t][d] = yv;
-        if (part == 1 && rec_ok)
-          st_elem(p.key_gate, kg_base + int64_t(t) * p.s_kg_pos + d, yv,
-                  p.kg_bf16);
-        s0 = s1;
-        s1 = s2;
-        s2 = s3;
+      for (int t = 0; t < QMAX; ++t) {
+        if (t < q) {
+          const float s3 = A::f(xs[jj][t]);
+          float acc = w[jj][0] * s0;
+          acc = fmaf(w[jj][1], s1, acc);
+          acc = fmaf(w[jj][2], s2, acc);
+          acc = fmaf(w[jj][3], s3, acc);
+          const float yv = acc * sigmoidf_(acc);
+          sm.y[part][t][d] = yv;
+          if (part == 1 && rec_ok) {
+            if (kg_bf16)
+              kg16[t * s_kp + d] = f32_to_bf16(yv);
+            else
+              kg32[t * s_kp + d] = yv;
+          }
+          s0 = s1;
+          s1 = s2;
+          s2 = s3;
+        }
+      }
+      // Roll: the two newest history entries, then the q new inputs, at
+      // the front; positions past 2 + q keep their bytes.
+      AT* csc = cs + ch * s_cc;
+      csc[0] = hist[jj][1];
+      csc[s_ct] = hist[jj][2];
+#pragma unroll
+      for (int t = 0; t < QMAX; ++t)
+        if (t < q) csc[(2 + t) * s_ct] = xs[jj][t];
+    }
+  }
+
+  // ---- second half of the state tile ---------------------------------------
+#pragma unroll
+  for (int pp = P0; pp < C::PASSES; ++pp)
+#pragma unroll
+    for (int c = 0; c < C::CHUNKS; ++c)
+      st[pp][c] = ld_stream(sbase + (pp * C::RPP + rg) * D + c * 4 * C::L +
+                            4 * lg);
+
+  // ---- phase 0d: gate decays, raw-gate record half, beta -------------------
+  const bool use_lb = (p.flags & kLowerBound) != 0;
+#pragma unroll
+  for (int jj = 0; jj < C::JG; ++jj) {
+    const int j = tid + jj * C::NT;
+    const int t = j / D, k = j - t * D;
+    if (t < q) {
+      const float g0 = A::f(gv[jj]);
+      sm.dec[t][k] = __expf(kda_gate(g0 + gb[jj], Ah, use_lb, p.lb));
+      if (rec_ok) {
+        if (kg_bf16)
+          kg16[t * s_kp + D + k] = f32_to_bf16(g0);
+        else
+          kg32[t * s_kp + D + k] = g0;
       }
     }
-    // Roll: the two newest history entries, then the q new inputs, at the
-    // front; positions past 2 + q keep their bytes.
-    csc[0] = h1;
-    csc[p.s_cs_tok] = h2;
-#pragma unroll
-    for (int t = 0; t < QMAX; ++t)
-      if (t < q) csc[int64_t(2 + t) * p.s_cs_tok] = xs[t];
   }
-
-  // ---- phase 0: gate decays, raw-gate record half, beta ----------------------
-  const float Ah = __expf(p.A_log[h]);
-  const bool use_lb = p.use_lb != 0;
-  const AT* graw = static_cast<const AT*>(p.raw_gate) + int64_t(bos) * p.s_g +
-                   int64_t(h) * D;
-  for (int j = tid; j < q * D; j += C::NT) {
-    const int t = j / D, k = j - t * D;
-    const float g0 = A::f(graw[int64_t(t) * p.s_g + k]);
-    const float x = g0 + p.dt_bias[int64_t(h) * D + k];
-    sm.dec[t][k] = __expf(kda_gate(x, Ah, use_lb, p.lb));
-    if (rec_ok)
-      st_elem(p.key_gate, kg_base + int64_t(t) * p.s_kg_pos + D + k, g0,
-              p.kg_bf16);
-  }
-  if (tid < q) {
-    const AT* rb = static_cast<const AT*>(p.raw_beta);
-    sm.beta[tid] = sigmoidf_(A::f(rb[int64_t(bos + tid) * p.s_beta + h]));
-  }
+  if (tid < q) sm.beta[tid] = sigmoidf_(A::f(bv));
+  if (tid == 0) sm.ticket[buf ^ 1] = drawn;
   lds_barrier();
 
-  // ---- phase 1: per-column partial sums, reduced per wave --------------------
-  const int wave = tid / 64, lane = tid % 64;
-  const bool col_ok = tid < D;
+  // Metadata of the next item: scalar loads in flight from here on.
+  advance();
+
+  // ---- phase 1: per-column partial sums, summed over columns in LDS ---------
+  const int col = tid % D;
+  const int grp = C::NG > 1 ? tid / D : 0;          // column group
+  const bool col_ok = tid < D || C::NG > 1;
   float kk[QMAX], qq[QMAX], dd[QMAX];
 #pragma unroll
   for (int t = 0; t < QMAX; ++t) {
     const bool ok = col_ok && t < q;
-    kk[t] = ok ? sm.y[1][t][tid] : 0.0f;
-    qq[t] = ok ? sm.y[0][t][tid] : 0.0f;
-    dd[t] = ok ? sm.dec[t][tid] : 1.0f;
+    kk[t] = ok ? sm.y[1][t][col] : 0.0f;
+    qq[t] = ok ? sm.y[0][t][col] : 0.0f;
+    dd[t] = ok ? sm.dec[t][col] : 1.0f;
   }
-  if (wave < C::CW) {
+#pragma unroll
+  for (int v0 = 0; v0 < C::NV; v0 += C::NB) {
+    // this thread's share of scalars [v0, v0 + NB)
+    auto put = [&](int idx, float val) {
+      if (idx >= v0 && idx < v0 + C::NB && idx % C::NG == grp && col_ok)
+        sm.part[(idx - v0) * D + col] = val;
+    };
 #pragma unroll
     for (int t = 0; t < QMAX; ++t) {
-      const float s1 = wave_sum(kk[t] * kk[t]);
-      const float s2 = wave_sum(qq[t] * qq[t]);
-      if (lane == 0) {
-        sm.red[wave][t] = s1;
-        sm.red[wave][QMAX + t] = s2;
-      }
+      put(t, kk[t] * kk[t]);
+      put(QMAX + t, qq[t] * qq[t]);
     }
 #pragma unroll
     for (int s = 0; s < QMAX; ++s) {
@@ -221,99 +333,99 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
       for (int t = s; t < QMAX; ++t) {
         if (t > s) {
           P *= dd[t];
-          const float m = wave_sum(kk[s] * P * kk[t]);
-          if (lane == 0) sm.red[wave][idx_m<QMAX>(t, s)] = m;
+          put(idx_m<QMAX>(t, s), kk[s] * P * kk[t]);
         }
-        const float n = wave_sum(kk[s] * P * qq[t]);
-        if (lane == 0) sm.red[wave][idx_n<QMAX>(t, s)] = n;
+        put(idx_n<QMAX>(t, s), kk[s] * P * qq[t]);
       }
     }
+    lds_barrier();
+    // chunk sums: scalar v, columns [c*CH, (c+1)*CH)
+    for (int task = tid; task < C::NB * C::NCH; task += C::NT) {
+      const int v = task / C::NCH, c = task - v * C::NCH;
+      if (v0 + v < C::NV) {
+        const f4* src =
+            reinterpret_cast<const f4*>(&sm.part[v * D + c * C::CH]);
+        f4 acc = src[0];
+#pragma unroll
+        for (int i = 1; i < C::CH / 4; ++i) acc += src[i];
+        sm.red[(v0 + v) * C::NCH + c] = (acc.x + acc.y) + (acc.z + acc.w);
+      }
+    }
+    lds_barrier();
   }
-  lds_barrier();
 
   // ---- phase 2: norms, column vectors, coefficient matrices ------------------
-  float rk[QMAX], rq[QMAX];
+  auto total = [&](int idx) {
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) s += sm.red[idx * C::NCH + c];
+    return s;
+  };
   const float inv_sqrt_d = 1.0f / sqrtf(float(D));
-#pragma unroll
-  for (int t = 0; t < QMAX; ++t) {
-    float sk = 0.0f, sq = 0.0f;
-#pragma unroll
-    for (int w = 0; w < C::CW; ++w) {
-      sk += sm.red[w][t];
-      sq += sm.red[w][QMAX + t];
-    }
-    rk[t] = rsqrtf(sk + kNormEps);
-    rq[t] = rsqrtf(sq + kNormEps) * inv_sqrt_d;
-  }
-  if (col_ok) {
+  if (tid < D) {
     float gam = 1.0f;
 #pragma unroll
     for (int t = 0; t < QMAX; ++t) {
       gam *= dd[t];
-      sm.vec[t][tid] = gam * kk[t] * rk[t];
-      sm.vec[QMAX + t][tid] = gam * qq[t] * rq[t];
+      const float rk = rsqrtf(total(t) + kNormEps);
+      const float rq = rsqrtf(total(QMAX + t) + kNormEps) * inv_sqrt_d;
+      sm.vec[t][tid] = gam * kk[t] * rk;
+      sm.vec[QMAX + t][tid] = gam * qq[t] * rq;
     }
   }
   for (int j = tid; j < QMAX * QMAX; j += C::NT) {
     const int t = j / QMAX, s = j - t * QMAX;
-    float m = 0.0f, n = 0.0f;
-#pragma unroll
-    for (int w = 0; w < C::CW; ++w) {
-      if (s < t) m += sm.red[w][idx_m<QMAX>(t, s)];
-      if (s <= t) n += sm.red[w][idx_n<QMAX>(t, s)];
-    }
-    // rk/rq were computed for every t by every thread above
-    float rks = 0.0f, rkt = 0.0f, rqt = 0.0f;
-#pragma unroll
-    for (int i = 0; i < QMAX; ++i) {
-      if (i == s) rks = rk[i];
-      if (i == t) {
-        rkt = rk[i];
-        rqt = rq[i];
-      }
-    }
-    sm.Mc[t][s] = m * rks * rkt;
-    sm.Nc[t][s] = n * rks * rqt;
+    const float rks = rsqrtf(total(s) + kNormEps);
+    const float rkt = rsqrtf(total(t) + kNormEps);
+    const float rqt = rsqrtf(total(QMAX + t) + kNormEps) * inv_sqrt_d;
+    sm.Mc[t][s] = s < t ? total(idx_m<QMAX>(t, s)) * rks * rkt : 0.0f;
+    sm.Nc[t][s] = s <= t ? total(idx_n<QMAX>(t, s)) * rks * rqt : 0.0f;
   }
   lds_barrier();
 
-  // ---- phase 3: 2Q dot products per state row --------------------------------
-  f4 ka[QMAX][C::CHUNKS], qa[QMAX][C::CHUNKS];
-#pragma unroll
-  for (int t = 0; t < QMAX; ++t)
-#pragma unroll
-    for (int c = 0; c < C::CHUNKS; ++c) {
-      const int col = c * 4 * C::L + 4 * lg;
-      ka[t][c] = *reinterpret_cast<const f4*>(&sm.vec[t][col]);
-      qa[t][c] = *reinterpret_cast<const f4*>(&sm.vec[QMAX + t][col]);
-    }
-#pragma unroll
-  for (int pp = 0; pp < C::PASSES; ++pp) {
-    float acc[2 * QMAX];
-#pragma unroll
-    for (int t = 0; t < QMAX; ++t) {
-      float sa = 0.0f, sb = 0.0f;
+  // ---- phase 3: 2q dot products per state row ---------------------------------
+  // Position-outer order: each position's two column vectors are read from
+  // LDS once and applied to every pass of the register-resident tile; the
+  // 2*PASSES partial sums of a lane are then reduced over its row group so
+  // that lane lg ends with row sum number lg >> (log2 L - log2 NVAL).
+  constexpr int SHIFT = (C::L == 16 ? 4 : C::L == 8 ? 3 : 2) -
+                        (C::NVAL == 16 ? 4 : C::NVAL == 8 ? 3
+                                         : C::NVAL == 4 ? 2
+                                         : C::NVAL == 2 ? 1 : 0);
+  const int vid = lg >> SHIFT;
+  float* dslot = &sm.part[((vid >> 1) * C::RPP + rg) * C::DS +
+                          (vid & 1) * QMAX];
+  // (kept rolled: one position's vectors live at a time)
+#pragma unroll 1
+  for (int t = 0; t < q; ++t) {
+    {
+      f4 ka[C::CHUNKS], qa[C::CHUNKS];
 #pragma unroll
       for (int c = 0; c < C::CHUNKS; ++c) {
-        const f4 s4 = st[pp][c];
-        sa = fmaf(s4.x, ka[t][c].x, sa);
-        sa = fmaf(s4.y, ka[t][c].y, sa);
-        sa = fmaf(s4.z, ka[t][c].z, sa);
-        sa = fmaf(s4.w, ka[t][c].w, sa);
-        sb = fmaf(s4.x, qa[t][c].x, sb);
-        sb = fmaf(s4.y, qa[t][c].y, sb);
-        sb = fmaf(s4.z, qa[t][c].z, sb);
-        sb = fmaf(s4.w, qa[t][c].w, sb);
+        const int cc = c * 4 * C::L + 4 * lg;
+        ka[c] = *reinterpret_cast<const f4*>(&sm.vec[t][cc]);
+        qa[c] = *reinterpret_cast<const f4*>(&sm.vec[QMAX + t][cc]);
       }
-      acc[t] = group_sum<C::L>(sa);
-      acc[QMAX + t] = group_sum<C::L>(sb);
-    }
-    if (lg == 0) {
-      float* drow = &sm.dots[(pp * C::RPP + rg) * C::DS];
+      float acc[C::NVAL];
 #pragma unroll
-      for (int i = 0; i < 2 * QMAX; i += 4)
-        *reinterpret_cast<f4*>(drow + i) =
-            f4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
+      for (int pp = 0; pp < C::PASSES; ++pp) {
+        float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int c = 0; c < C::CHUNKS; ++c) {
+          const f4 s4 = st[pp][c];
+          sa = fmaf(s4.x, ka[c].x, sa);
+          sa = fmaf(s4.y, ka[c].y, sa);
+          sa = fmaf(s4.z, ka[c].z, sa);
+          sa = fmaf(s4.w, ka[c].w, sa);
+          sb = fmaf(s4.x, qa[c].x, sb);
+          sb = fmaf(s4.y, qa[c].y, sb);
+          sb = fmaf(s4.z, qa[c].z, sb);
+          sb = fmaf(s4.w, qa[c].w, sb);
+        }
+        acc[2 * pp] = sa;
+        acc[2 * pp + 1] = sb;
+      }
+      dslot[t] = transpose_sum<C::L, C::NVAL>(acc, lg);
     }
   }
   lds_barrier();
@@ -321,59 +433,133 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
   // ---- phase 4: per-row triangular solve, outputs and corrections -------------
   if (tid < D) {
     const int v = tid;
+    float* __restrict__ corr = p.correction + int64_t(it.r) * p.s_c_row +
+                               int64_t(h) * p.s_c_head + v;
+    const int64_t ob = int64_t(it.bos) * p.s_out + h * D + v;
+    const int s_cp = p.s_c_pos, s_out = p.s_out;
+    const float* drow = &sm.part[v * C::DS];
     float cc[QMAX];
 #pragma unroll
     for (int t = 0; t < QMAX; ++t) {
       if (t < q) {
-        float u = sm.dots[v * C::DS + t];
+        float u = drow[t];
 #pragma unroll
         for (int s = 0; s < t; ++s) u = fmaf(sm.Mc[t][s], cc[s], u);
         cc[t] = sm.beta[t] * (sm.y[2][t][v] - u);
-        float o = sm.dots[v * C::DS + QMAX + t];
+        float o = drow[QMAX + t];
 #pragma unroll
         for (int s = 0; s <= t; ++s) o = fmaf(sm.Nc[t][s], cc[s], o);
-        st_elem(p.out, int64_t(bos + t) * p.s_out + out_col + v, o,
-                p.out_bf16);
-        if (rec_ok)
-          p.correction[int64_t(r) * p.s_c_row + int64_t(h) * p.s_c_head +
-                       int64_t(t) * p.s_c_pos + v] = cc[t];
+        if (p.flags & kOutBf16)
+          static_cast<uint16_t*>(p.out)[ob + t * s_out] = f32_to_bf16(o);
+        else
+          static_cast<float*>(p.out)[ob + t * s_out] = o;
+        if (rec_ok) corr[t * s_cp] = cc[t];
       }
     }
   }
 }
 
 template <int D, int QMAX, bool ACT_BF16>
-__global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT))
+__global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
+                                  (VerifyCfg<D, QMAX>::MIN_WAVES))
     kda_verify_kernel(VerifyParams p) {
+  using C = VerifyCfg<D, QMAX>;
   __shared__ VerifySmem<D, QMAX> sm;
   const int tid = threadIdx.x;
-  // Ticket protocol: every workgroup draws tickets until one is past the
-  // last item, prefetching the next ticket while it works on the current
-  // one.  Exactly n_items + gridDim.x draws happen in total, so the draw
-  // that returns the largest value is the last one; its workgroup resets
-  // the counter for the next launch on the stream.
+  // Ticket protocol: a ticket claims per_ticket consecutive items.  Every
+  // workgroup draws tickets until one is past the last, drawing the next
+  // ticket while it works on the last item of its current chunk.  Exactly
+  // n_tickets + gridDim.x draws happen in total, so the draw that returns
+  // the largest value is the last one; its workgroup resets the counter for
+  // the next launch on the stream.
   if (tid == 0) sm.ticket[0] = atomicAdd(p.counter, 1);
   lds_barrier();
   int ticket = uniform(sm.ticket[0]);
+  int item = ticket * p.per_ticket;
+  int end = min(item + p.per_ticket, p.n_items);
+  Item it{};
+  if (ticket < p.n_tickets) it = load_item(p, uniform(item / p.H), uniform(item % p.H));
   int buf = 0;
-  while (ticket < p.n_items) {
-    int next = 0;
-    if (tid == 0) next = atomicAdd(p.counter, 1);
-    const int b = uniform(ticket / p.H);
-    const int h = uniform(ticket - b * p.H);
-    verify_item<D, QMAX, ACT_BF16>(p, sm, b, h);
-    buf ^= 1;
-    if (tid == 0) sm.ticket[buf] = next;
+  while (ticket < p.n_tickets) {
+    const bool last = item + 1 >= end;
+    int drawn = 0;
+    if (last && tid == 0) drawn = atomicAdd(p.counter, 1);
+    int nticket = ticket, nitem = item + 1, nend = end;
+    Item nx{};
+    auto advance = [&]() {
+      if (last) {
+        nticket = uniform(sm.ticket[buf ^ 1]);
+        nitem = nticket * p.per_ticket;
+        nend = min(nitem + p.per_ticket, p.n_items);
+      }
+      if (nticket < p.n_tickets) nx = load_item(p, uniform(nitem / p.H),
+                                                 uniform(nitem % p.H));
+    };
+    if (it.live) {
+      if (it.q == QMAX)
+        verify_item<D, QMAX, ACT_BF16, true>(p, sm, it, drawn, buf, advance);
+      else
+        verify_item<D, QMAX, ACT_BF16, false>(p, sm, it, drawn, buf,
+                                              advance);
+    } else {
+      // Null block: zero outputs, touch no state, record or conv byte.
+      for (int j = tid; j < it.q * D; j += C::NT) {
+        const int t = j / D, v = j - t * D;
+        st_elem(p.out, int64_t(it.bos + t) * p.s_out + int64_t(it.h) * D + v,
+                0.0f, (p.flags & kOutBf16) != 0);
+      }
+      if (tid == 0) sm.ticket[buf ^ 1] = drawn;
+    }
     lds_barrier();
-    ticket = uniform(sm.ticket[buf]);
+    if (!it.live) advance();
+    buf ^= 1;
+    ticket = nticket;
+    item = nitem;
+    end = nend;
+    it = nx;
   }
-  if (tid == 0 && ticket == p.n_items + int(gridDim.x) - 1)
+  if (tid == 0 && ticket == p.n_tickets + int(gridDim.x) - 1)
     atomicExch(p.counter, 0);
 }
 
+// One workgroup per (head, request) item: blockIdx.x = head, blockIdx.y =
+// request, so the hardware dispatcher hands out items in request-major
+// order and refills each compute unit as workgroups retire (which also
+// balances ragged windows).  No loop-carried state, no ticket counter.
+template <int D, int QMAX, bool ACT_BF16>
+__global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
+                                  (VerifyCfg<D, QMAX>::MIN_WAVES))
+    kda_verify_grid_kernel(VerifyParams p) {
+  using C = VerifyCfg<D, QMAX>;
+  __shared__ VerifySmem<D, QMAX> sm;
+  const Item it = load_item(p, int(blockIdx.y), int(blockIdx.x));
+  auto advance = [] {};
+  if (it.live) {
+    if (it.q == QMAX)
+      verify_item<D, QMAX, ACT_BF16, true>(p, sm, it, 0, 0, advance);
+    else
+      verify_item<D, QMAX, ACT_BF16, false>(p, sm, it, 0, 0, advance);
+  } else {
+    // Null block: zero outputs, touch no state, record or conv byte.
+    for (int j = threadIdx.x; j < it.q * D; j += C::NT) {
+      const int t = j / D, v = j - t * D;
+      st_elem(p.out, int64_t(it.bos + t) * p.s_out + int64_t(it.h) * D + v,
+              0.0f, (p.flags & kOutBf16) != 0);
+    }
+  }
+}
+
+// grid <= 0: one workgroup per item (the default).  grid > 0: a persistent
+// grid of at most `grid` workgroups drawing tickets from p.counter (also
+// used when the batch exceeds the 65535 requests a grid row can address).
 template <int D, int QMAX, bool ACT_BF16>
 int launch_one(const VerifyParams& p, int grid, hipStream_t stream) {
   using C = VerifyCfg<D, QMAX>;
+  if (grid <= 0 && p.B <= 65535) {
+    hipLaunchKernelGGL((kda_verify_grid_kernel<D, QMAX, ACT_BF16>),
+                       dim3(p.H, p.B), dim3(C::NT), 0, stream, p);
+    return int(hipGetLastError());
+  }
   auto kern = kda_verify_kernel<D, QMAX, ACT_BF16>;
   if (grid <= 0) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -387,8 +573,12 @@ int launch_one(const VerifyParams& p, int grid, hipStream_t stream) {
     if (e != hipSuccess) return int(e);
     grid = max(1, cus * max(per_cu, 1));
   }
-  grid = min(grid, p.n_items);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, stream, p);
+  if (p.counter == nullptr) return int(hipErrorInvalidValue);
+  VerifyParams q = p;
+  if (q.per_ticket <= 0) q.per_ticket = 1;
+  q.n_tickets = (q.n_items + q.per_ticket - 1) / q.per_ticket;
+  grid = min(grid, q.n_tickets);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, stream, q);
   return int(hipGetLastError());
 }
 

@@ -83,7 +83,7 @@ def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
                 conv_weight, query_start_loc, state_indices,
                 num_accepted_tokens, spec_query_len, conv_dim_first,
                 work_counter, record_rows=None, null_block_id=0,
-                max_workgroups=0) -> _abi.KdaVerifyArgs:
+                max_workgroups=0, items_per_ticket=0) -> _abi.KdaVerifyArgs:
     a = _abi.KdaVerifyArgs()
     a.mixed_qkv = describe(mixed_qkv)
     a.raw_gate = describe(raw_gate)
@@ -108,6 +108,7 @@ def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
     a.use_lower_bound = 0 if lower_bound is None else 1
     a.lower_bound = 0.0 if lower_bound is None else float(lower_bound)
     a.max_workgroups = max_workgroups
+    a.items_per_ticket = items_per_ticket
     return a
 
 
@@ -225,7 +226,7 @@ class CommitContext:
              for L in layers], dtype=torch.float32, device=dev)
 
     def args(self, state_indices, commit_lens, final_state_indices=None,
-             record_rows=None) -> _abi.KdaCommitArgs:
+             record_rows=None, max_workgroups=0) -> _abi.KdaCommitArgs:
         a = _abi.KdaCommitArgs()
         a.num_layers = self.num_layers
         a.batch = state_indices.shape[0]
@@ -247,6 +248,7 @@ class CommitContext:
         a.correction_strides[:] = list(self.correction_strides)
         a.key_gate_strides[:] = list(self.key_gate_strides)
         a.key_gate_dtype = self.key_gate_dtype
+        a.max_workgroups = max_workgroups
         a.A_log = self.A_log.data_ptr()
         a.A_log_strides[:] = list(self.A_log.stride())
         a.dt_bias = self.dt_bias.data_ptr()
@@ -268,11 +270,12 @@ class CommitContext:
         return _abi.load().kda_check_commit(ctypes.byref(a))
 
     def commit(self, state_indices, commit_lens, final_state_indices=None,
-               record_rows=None, stream=None) -> None:
+               record_rows=None, stream=None, max_workgroups=0) -> None:
         """Fold the first commit_lens[b] recorded positions of every request
-        into its checkpoint (or final slot), for all layers, in one launch."""
+        into its checkpoint (or final slot), for all layers, in one launch.
+        max_workgroups > 0 selects the persistent strided schedule."""
         a = self.args(state_indices, commit_lens, final_state_indices,
-                      record_rows)
+                      record_rows, max_workgroups)
         rc = _abi.load().kda_recoverssm_commit(ctypes.byref(a),
                                               _stream(stream))
         if rc != _abi.KDA_OK:

@@ -156,6 +156,12 @@ def test_capacity_and_argument_errors():
     assert _code(kw) == _abi.KDA_E_CAPACITY
     wl, kw = _kw()
     kw["work_counter"] = None
+    assert _code(kw) == 0            # the default schedule has no counter
+    kw["max_workgroups"] = 8
+    assert _code(kw) == _abi.KDA_E_ARG
+    kw["max_workgroups"] = -1        # negative: default schedule
+    assert _code(kw) == 0
+    kw["items_per_ticket"] = -2
     assert _code(kw) == _abi.KDA_E_ARG
 
 

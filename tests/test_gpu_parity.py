@@ -260,10 +260,12 @@ def test_results_independent_of_grid_size():
     L = wl.layers[0]
     page0, rec0 = L.page.clone(), None
     outs = []
-    for grid in (1, 3, 0):
+    for grid, per in ((1, 0), (3, 0), (0, 0), (0, 3), (5, 7), (2, 1000)):
         L.page.copy_(page0)
-        drive.verify(wl, 0, _counter(), max_workgroups=grid)
+        c = _counter()
+        drive.verify(wl, 0, c, max_workgroups=grid, items_per_ticket=per)
         torch.cuda.synchronize()
+        assert int(c.item()) == 0
         outs.append((L.out.clone(), L.page.clone()))
     for o, p in outs[1:]:
         assert np.array_equal(bits(o), bits(outs[0][0]))
@@ -374,3 +376,24 @@ def test_deferred_sequence_sampled():
         torch.cuda.synchronize()
         errs = check_verify(wl, layer, s1, ref1)
         print("deferred", layer, errs)
+
+
+def test_commit_schedules_agree_bitwise():
+    # The persistent strided schedule and the one-workgroup-per-item grid
+    # compute every item with the same code: identical bytes.
+    wl = make_workload("large", DEV, B=24, H=4, D=128, N=40,
+                       gates=[None, -5.0, None])
+    for layer in range(3):
+        drive.verify(wl, layer, _counter())
+    ctx = drive.commit_context(wl)
+    pages0 = [L.page.clone() for L in wl.layers]
+    results = []
+    for grid in (0, 7, 1, 100000):
+        for L, p0 in zip(wl.layers, pages0):
+            L.page.copy_(p0)
+        ctx.commit(wl.state_indices, wl.commit_lens, max_workgroups=grid)
+        torch.cuda.synchronize()
+        results.append([L.page.clone() for L in wl.layers])
+    for other in results[1:]:
+        for a, b in zip(results[0], other):
+            assert torch.equal(a, b)
