@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 /* Status codes. */
 typedef enum {
@@ -85,6 +85,17 @@ typedef enum {
 
 /* Element types. */
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* How the verify hands out its (request, head) work items. */
+typedef enum {
+  KDA_SCHEDULE_DEFAULT = 0,    /* the library's choice (the fastest measured
+                                  for the shape) */
+  KDA_SCHEDULE_PER_ITEM = 1,   /* one workgroup per item, handed out by the
+                                  hardware dispatcher in request-major order */
+  KDA_SCHEDULE_TICKETS = 2     /* persistent workgroups drawing tickets of
+                                  items_per_ticket items from work_counter
+                                  (the kernels page's design) */
+} kda_schedule;
 
 /* A strided tensor view.  `stride` is in elements; unused trailing entries
    of shape/stride are ignored. */
@@ -125,26 +136,23 @@ typedef struct {
   const int32_t* num_accepted_tokens;  /* [batch] conv history offset + 1 */
   const int32_t* record_rows;          /* [batch] record row, or NULL: the
                                           request's state slot */
-  int32_t* work_counter;   /* device int32[1]: ticket counter of the
-                              persistent schedule (max_workgroups > 0, or a
-                              batch above 65535).  Must be 0 before the first
-                              launch; every launch leaves it at 0.  One
-                              counter per launch in flight.  May be NULL when
-                              the persistent schedule is not used. */
+  int32_t* work_counter;   /* device int32[1]: ticket counter of the ticket
+                              schedule.  Must be 0 before the first launch;
+                              every launch leaves it at 0.  One counter per
+                              launch in flight.  May be NULL for the other
+                              schedules. */
   int32_t batch;
   int32_t spec_query_len;  /* Q */
   int32_t null_block_id;   /* slots <= this are null (0 in vLLM) */
   int32_t conv_dim_first;  /* 1: conv_state is [N, 3HD, Lc]; 0: [N, Lc, 3HD] */
   int32_t use_lower_bound; /* 1: g = lower_bound*sigmoid(A x); 0: softplus */
   float lower_bound;
-  int32_t max_workgroups;  /* 0: one workgroup per (request, head), handed
-                              out by the hardware dispatcher in request-major
-                              order (the default, and the fastest measured);
-                              > 0: a persistent grid of at most this many
-                              workgroups that draw (request, head) items
-                              from work_counter */
-  int32_t items_per_ticket; /* (request, head) items claimed per ticket;
-                               0 = library default */
+  int32_t max_workgroups;  /* ticket schedule: at most this many
+                              workgroups (0 = as many as are resident at
+                              once); ignored by the per-item schedule */
+  int32_t items_per_ticket; /* ticket schedule: (request, head) items
+                               claimed per ticket; 0 = library default */
+  int32_t schedule;        /* kda_schedule */
 } kda_verify_args;
 
 /* Arguments of kda_recoverssm_commit.  Per-layer tensors are described by

@@ -20,6 +20,10 @@ KDA_E_CAPACITY = 6
 KDA_E_DEVICE = 7
 KDA_E_ARG = 8
 
+KDA_SCHEDULE_DEFAULT = 0
+KDA_SCHEDULE_PER_ITEM = 1
+KDA_SCHEDULE_TICKETS = 2
+
 KDA_F32 = 0
 KDA_BF16 = 1
 
@@ -50,6 +54,7 @@ class KdaVerifyArgs(Structure):
         ("null_block_id", c_int32), ("conv_dim_first", c_int32),
         ("use_lower_bound", c_int32), ("lower_bound", c_float),
         ("max_workgroups", c_int32), ("items_per_ticket", c_int32),
+        ("schedule", c_int32),
     ]
 
 

@@ -74,6 +74,7 @@ struct VerifyPlan {
   bool act_bf16 = false;
   bool noop = false;
   int grid = 0;
+  int schedule = 0;
 };
 
 #define KDA_TRY(expr)             \
@@ -260,13 +261,17 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
   // Metadata.
   if (a->items_per_ticket < 0)
     return fail(KDA_E_ARG, "items_per_ticket is negative");
+  if (a->max_workgroups < 0)
+    return fail(KDA_E_ARG, "max_workgroups is negative");
+  if (a->schedule < KDA_SCHEDULE_DEFAULT || a->schedule > KDA_SCHEDULE_TICKETS)
+    return fail(KDA_E_ARG, "unknown schedule %d", a->schedule);
   if (a->batch > 0) {
     if (!a->query_start_loc || !a->state_indices || !a->num_accepted_tokens)
       return fail(KDA_E_ARG,
                   "query_start_loc, state_indices and num_accepted_tokens "
                   "are required");
-    if (!a->work_counter && (a->max_workgroups > 0 || a->batch > 65535))
-      return fail(KDA_E_ARG, "the persistent schedule needs a work_counter");
+    if (!a->work_counter && a->schedule == KDA_SCHEDULE_TICKETS)
+      return fail(KDA_E_ARG, "the ticket schedule needs a work_counter");
     const void* ptrs[] = {a->query_start_loc, a->state_indices,
                           a->num_accepted_tokens, a->record_rows,
                           a->work_counter};
@@ -341,6 +346,10 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
             (a->key_gate.dtype == KDA_BF16 ? kda::kKgBf16 : 0) |
             (a->conv_weight.dtype == KDA_BF16 ? kda::kWBf16 : 0) |
             (a->use_lower_bound ? kda::kLowerBound : 0);
+  if (a->conv_dim_first && s_tok == 1 && (Q == 4 || Q == 8 || Q == 16) &&
+      (Lc * ea) % 4 == 0 && (s_chan * ea) % 4 == 0 &&
+      (cs.stride[0] * ea) % 4 == 0)
+    p.flags |= kda::kConvRow;
   p.lb = a->lower_bound;
   p.n_items = int32_t(int64_t(a->batch) * H);
   p.per_ticket = a->items_per_ticket;
@@ -348,6 +357,7 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
   plan->act_bf16 = act == KDA_BF16;
   plan->noop = a->batch == 0 || T == 0;
   plan->grid = a->max_workgroups;
+  plan->schedule = a->schedule;
   return KDA_OK;
 }
 
@@ -496,7 +506,8 @@ int kda_conv_update_verify(const kda_verify_args* args, void* stream) {
   KDA_TRY(plan_verify(args, &plan));
   if (plan.noop) return KDA_OK;
   return device_status(
-      kda::launch_verify(plan.p, plan.D, plan.act_bf16, plan.grid,
+      kda::launch_verify(plan.p, plan.D, plan.act_bf16, plan.schedule,
+                         plan.grid,
                          static_cast<hipStream_t>(stream)),
       "kda_conv_update_verify launch");
 }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -49,6 +51,69 @@ struct Act<false> {
   typedef float T;
   static __device__ __forceinline__ float f(T x) { return x; }
 };
+
+// ---- addressing ------------------------------------------------------------------
+
+// Element `off` of a wave-uniform base pointer, with the offset taken as an
+// unsigned 32-bit byte count (the host checks that every in-item offset
+// fits).  Written this way the compiler can use the scalar-base + 32-bit
+// vector-offset form of global memory instructions, which keeps one VGPR
+// per address instead of two.
+template <class T>
+__device__ __forceinline__ T& at(T* base, uint32_t off) {
+  using C = typename std::conditional<std::is_const<T>::value, const char,
+                                      char>::type;
+  return *reinterpret_cast<T*>(reinterpret_cast<C*>(base) +
+                               off * uint32_t(sizeof(T)));
+}
+
+// Scalar loads of values the kernel never writes (per-request metadata,
+// per-head parameters) at wave-uniform addresses, with their own wait.
+// Written out because inside a persistent loop that also stores to global
+// memory the compiler cannot prove these locations unclobbered and would
+// use vector loads, whose completion waits (in order) behind the state tile
+// streaming in for the next item.  All addresses must be 4-byte aligned.
+// A pointer the compiler must keep in scalar registers (an inline-asm "s"
+// operand is not moved out of vector registers by itself).
+__device__ __forceinline__ const int32_t* sgpr_ptr(const int32_t* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  return reinterpret_cast<const int32_t*>((uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ void sload4(const int32_t* a0, const int32_t* a1,
+                                       const int32_t* a2, const int32_t* a3,
+                                       int32_t& v0, int32_t& v1, int32_t& v2,
+                                       int32_t& v3) {
+  a0 = sgpr_ptr(a0);
+  a1 = sgpr_ptr(a1);
+  a2 = sgpr_ptr(a2);
+  a3 = sgpr_ptr(a3);
+  asm volatile(
+      "s_load_dword %0, %4, 0x0\n\t"
+      "s_load_dword %1, %5, 0x0\n\t"
+      "s_load_dword %2, %6, 0x0\n\t"
+      "s_load_dword %3, %7, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      // early-clobber: a result register must not alias an address that a
+      // later load of the sequence still reads
+      : "=&s"(v0), "=&s"(v1), "=&s"(v2), "=&s"(v3)
+      : "s"(a0), "s"(a1), "s"(a2), "s"(a3)
+      : "memory");
+}
+
+__device__ __forceinline__ int32_t sload1(const int32_t* a0) {
+  a0 = sgpr_ptr(a0);
+  int32_t v0;
+  asm volatile(
+      "s_load_dword %0, %1, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(v0)
+      : "s"(a0)
+      : "memory");
+  return v0;
+}
 
 // ---- streaming 16-byte accesses (state rows are touched once) -----------------
 
@@ -150,6 +215,16 @@ __device__ __forceinline__ float wave_sum(float v) {
          __int_as_float(__builtin_amdgcn_readlane(b, 16)) +
          __int_as_float(__builtin_amdgcn_readlane(b, 32)) +
          __int_as_float(__builtin_amdgcn_readlane(b, 48));
+}
+
+// threadIdx.x as a value the compiler must treat as new at every call.
+// Inside a persistent loop, lane offsets derived from it would otherwise be
+// hoisted out of the loop and kept live (or spilled) across it; recomputing
+// them per item costs a few instructions.
+__device__ __forceinline__ int fresh_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
 }
 
 __device__ __forceinline__ int uniform(int x) {

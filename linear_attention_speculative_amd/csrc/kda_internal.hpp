@@ -48,6 +48,9 @@ constexpr int32_t kOutBf16 = 1;
 constexpr int32_t kKgBf16 = 2;
 constexpr int32_t kWBf16 = 4;
 constexpr int32_t kLowerBound = 8;
+// dim-first conv state whose rows (Q + 2 elements, Q in {4, 8, 16}) are
+// contiguous and 4-byte aligned: read and rolled a whole row at a time
+constexpr int32_t kConvRow = 16;
 
 struct CommitParams {
   const int64_t* state_base;  const int64_t* state_bs;
@@ -70,9 +73,15 @@ struct CommitParams {
   int32_t grid;   // <= 0: one workgroup per item; > 0: persistent, strided
 };
 
-// Launchers (return a hipError_t as int).  `grid` <= 0 means the default.
-int launch_verify(const VerifyParams& p, int D, bool act_bf16, int grid,
-                  hipStream_t stream);
+// Verify schedules (kda_schedule of the public header).
+constexpr int kScheduleDefault = 0;
+constexpr int kSchedulePerItem = 1;
+constexpr int kScheduleTickets = 2;
+
+// Launchers (return a hipError_t as int).  `grid` <= 0: as many persistent
+// workgroups as are resident at once.
+int launch_verify(const VerifyParams& p, int D, bool act_bf16, int schedule,
+                  int grid, hipStream_t stream);
 int launch_commit(const CommitParams& p, int D, hipStream_t stream);
 int launch_reset_counter(int32_t* counter, int n, hipStream_t stream);
 

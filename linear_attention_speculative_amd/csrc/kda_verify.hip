@@ -42,6 +42,8 @@
 //      reduction over the lanes that share a row; row results to LDS.
 //   4  one thread per row: triangular solve for c_t, outputs o_t; stores of
 //      out and of the correction record (coalesced along V).
+#include <utility>
+
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -108,144 +110,184 @@ __device__ __forceinline__ constexpr int idx_n(int t, int s) {
 // Wave-uniform description of one (request, head) work item.
 struct Item {
   int b, h, bos, q, slot, r, a;
-  bool live, rec_ok;
+  bool valid, live, rec_ok;
 };
+
+// The item past the end of a schedule: no view of it holds any byte.
+__device__ __forceinline__ Item no_item() {
+  Item it{};
+  it.valid = false;
+  it.live = false;
+  it.rec_ok = false;
+  return it;
+}
 
 __device__ __forceinline__ Item load_item(const VerifyParams& p, int b,
                                           int h) {
   Item it;
+  it.valid = true;
   it.b = b;
   it.h = h;
+  int bos, eos, slot, acc;
+  sload4(p.qsl + b, p.qsl + b + 1, p.slots + b, p.accepted + b, bos, eos,
+         slot, acc);
   // Token rows outside [0, T) are never touched (memory-safety clamp).
-  it.bos = p.qsl[it.b];
-  const int eos = p.qsl[it.b + 1];
-  it.q = (it.bos < 0 || it.bos >= p.T)
-             ? 0
-             : min(min(max(eos - it.bos, 0), p.Q), p.T - it.bos);
-  it.slot = p.slots[it.b];
-  it.live = it.q > 0 && it.slot > p.null_id && it.slot >= 0 &&
-            it.slot < p.N;
-  it.a = min(max(p.accepted[it.b], 1), p.Q);
-  it.r = p.record_rows ? p.record_rows[it.b] : it.slot;
+  it.bos = bos;
+  it.q = (bos < 0 || bos >= p.T) ? 0
+                                 : min(min(max(eos - bos, 0), p.Q), p.T - bos);
+  it.slot = slot;
+  it.live = it.q > 0 && slot > p.null_id && slot >= 0 && slot < p.N;
+  it.a = min(max(acc, 1), p.Q);
+  it.r = p.record_rows ? sload1(p.record_rows + b) : slot;
   it.rec_ok = it.r >= 0 && it.r < p.R;
   return it;
 }
 
-// One live item.  `drawn` is thread 0's freshly drawn ticket (meaningful
-// on the last item of a chunk); it is published through LDS at the first
-// barrier, after which `advance()` lets every thread start the scalar loads
-// of the next item's metadata early.
+// Per-head constants, raw: conv taps of the head's 3D channels (f32 bits,
+// or a bf16 in the low half), dt_bias, A_log.
+template <int D, int QMAX>
+struct HeadRegs {
+  using C = VerifyCfg<D, QMAX>;
+  uint32_t w[C::JC][4];
+  float gb[C::JG];
+  float alog;
+};
+
+// Raw registers of one item's small loads: conv history, new inputs, gate
+// inputs, beta.  Conversions happen where the values are used, so that no
+// instruction waits for these loads where they are issued.
+template <int D, int QMAX, bool ACT_BF16>
+struct Small {
+  using C = VerifyCfg<D, QMAX>;
+  using AT = typename Act<ACT_BF16>::T;
+  // dwords of one channel's conv-state row (QMAX + 2 elements)
+  static constexpr int RD = (QMAX + 2) * int(sizeof(AT)) / 4;
+  AT hist[C::JC][3];        // history, element by element
+  uint32_t row[C::JC][RD];  // or the whole row (contiguous-row layout)
+  AT xs[C::JC][QMAX];
+  AT gv[C::JG];
+  AT bv;
+};
+
+// The state tile of one item in registers: lane lg of row group rg holds
+// rows pp * RPP + rg, columns c * 4L + 4 lg .. + 3.
+template <int D, int QMAX>
+using Tile = f4[VerifyCfg<D, QMAX>::PASSES][VerifyCfg<D, QMAX>::CHUNKS];
+
+template <int D, int QMAX>
+__device__ __forceinline__ void load_head(const VerifyParams& p, int h,
+                                          HeadRegs<D, QMAX>& hr) {
+  using C = VerifyCfg<D, QMAX>;
+  const int tid = fresh_tid();
+  const int HD = p.H * D;
+  const bool w_bf16 = (p.flags & kWBf16) != 0;
+#pragma unroll
+  for (int jj = 0; jj < C::JC; ++jj) {
+    const int j = tid + jj * C::NT;
+    if (j < 3 * D) {
+      const int part = j / D, d = j - part * D;
+      const uint32_t wo = (part * HD + h * D + d) * p.s_w_chan;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t o = wo + i * p.s_w_tap;
+        hr.w[jj][i] =
+            w_bf16 ? uint32_t(at(static_cast<const uint16_t*>(p.conv_weight), o))
+                   : at(static_cast<const uint32_t*>(p.conv_weight), o);
+      }
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < C::JG; ++jj)
+    hr.gb[jj] = at(p.dt_bias + h * D, uint32_t((tid + jj * C::NT) % D));
+  hr.alog = __int_as_float(sload1(reinterpret_cast<const int32_t*>(p.A_log) + h));
+}
+
+// Element E of a conv-state row held as dwords.
+template <class AT, int E, int RD>
+__device__ __forceinline__ AT row_elem(const uint32_t (&rw)[RD]) {
+  if constexpr (sizeof(AT) == 2)
+    return AT((rw[E / 2] >> (16 * (E % 2))) & 0xffffu);
+  else
+    return __uint_as_float(rw[E]);
+}
+
+// Element o + I of the row for a wave-uniform o in [0, QMAX - 1].
+template <class AT, int I, int QMAX, int RD>
+__device__ __forceinline__ AT row_at(const uint32_t (&rw)[RD], int o) {
+  AT v = row_elem<AT, I>(rw);
+  [&]<int... K>(std::integer_sequence<int, K...>) {
+    ((v = (o == K + 1) ? row_elem<AT, I + K + 1>(rw) : v), ...);
+  }(std::make_integer_sequence<int, QMAX - 1>{});
+  return v;
+}
+
+template <class AT>
+__device__ __forceinline__ uint32_t bits_of(AT v) {
+  if constexpr (sizeof(AT) == 2)
+    return uint32_t(v);
+  else
+    return __float_as_uint(v);
+}
+
+// Phase 0 of a live item: conv + SiLU of the head's 3D channels, key
+// record, conv roll; `mid()` runs between the conv and the gate (the
+// one-workgroup-per-item kernel issues the second half of its tile there);
+// gate decays, raw-gate record half, sigmoid(beta).
 // FULL: the request verifies all QMAX positions (q == QMAX), so every
 // position guard folds away at compile time.
-template <int D, int QMAX, bool ACT_BF16, bool FULL, class Advance>
-__device__ __forceinline__ void verify_item(const VerifyParams& p,
-                                            VerifySmem<D, QMAX>& sm,
-                                            const Item& it, int drawn,
-                                            int buf, Advance&& advance) {
+template <int D, int QMAX, bool ACT_BF16, bool FULL, class Mid>
+__device__ __forceinline__ void item_front(const VerifyParams& p,
+                                           VerifySmem<D, QMAX>& sm,
+                                           const Item& it,
+                                           const Small<D, QMAX, ACT_BF16>& s,
+                                           const HeadRegs<D, QMAX>& hr,
+                                           Mid&& mid) {
   using C = VerifyCfg<D, QMAX>;
   using A = Act<ACT_BF16>;
   using AT = typename A::T;
-  const int tid = threadIdx.x;
+  const int tid = fresh_tid();
   const int h = it.h;
   const int q = FULL ? QMAX : it.q;
   const bool rec_ok = it.rec_ok;
   const int HD = p.H * D;
-
-  // Wave-uniform 64-bit bases of everything this item touches; lanes add
-  // 32-bit offsets (the host checks that in-item offsets fit).
-  const AT* __restrict__ xq =
-      static_cast<const AT*>(p.mixed_qkv) + int64_t(it.bos) * p.s_x;
   AT* __restrict__ cs =
       static_cast<AT*>(p.conv_state) + int64_t(it.slot) * p.s_cs_slot;
-  const AT* __restrict__ graw = static_cast<const AT*>(p.raw_gate) +
-                                int64_t(it.bos) * p.s_g + h * D;
-  const AT* __restrict__ rbeta = static_cast<const AT*>(p.raw_beta) +
-                                 int64_t(it.bos) * p.s_beta + h;
   const int64_t kg_off =
       int64_t(it.r) * p.s_kg_row + int64_t(h) * p.s_kg_head;
   float* __restrict__ kg32 = static_cast<float*>(p.key_gate) + kg_off;
   uint16_t* __restrict__ kg16 = static_cast<uint16_t*>(p.key_gate) + kg_off;
-  const int s_x = p.s_x, s_g = p.s_g, s_beta = p.s_beta;
   const int s_cc = p.s_cs_chan, s_ct = p.s_cs_tok;
   const int s_kp = p.s_kg_pos;
   const bool kg_bf16 = (p.flags & kKgBf16) != 0;
+  const bool w_bf16 = (p.flags & kWBf16) != 0;
+  const bool row_fast = (p.flags & kConvRow) != 0;
 
-  // ---- phase 0a: small loads first -------------------------------------------
-  AT hist[C::JC][3];
-  AT xs[C::JC][QMAX];
-  float w[C::JC][4];
 #pragma unroll
   for (int jj = 0; jj < C::JC; ++jj) {
     const int j = tid + jj * C::NT;
     if (j < 3 * D) {
       const int part = j / D, d = j - part * D;
       const int ch = part * HD + h * D + d;
-      const int co = ch * s_cc + (it.a - 1) * s_ct;
+      float w[4];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) hist[jj][i] = cs[co + i * s_ct];
-      const int wo = ch * p.s_w_chan;
-      const int wt = p.s_w_tap;
-      if (p.flags & kWBf16) {
-        const uint16_t* wp = static_cast<const uint16_t*>(p.conv_weight) + wo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[jj][i] = bf16_to_f32(wp[i * wt]);
-      } else {
-        const float* wp = static_cast<const float*>(p.conv_weight) + wo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[jj][i] = wp[i * wt];
+      for (int i = 0; i < 4; ++i)
+        w[i] = __uint_as_float(w_bf16 ? hr.w[jj][i] << 16 : hr.w[jj][i]);
+      // history: positions a-1 .. a+1 of the conv state
+      AT h0 = s.hist[jj][0], h1 = s.hist[jj][1], h2 = s.hist[jj][2];
+      if (row_fast) {
+        h0 = row_at<AT, 0, QMAX>(s.row[jj], it.a - 1);
+        h1 = row_at<AT, 1, QMAX>(s.row[jj], it.a - 1);
+        h2 = row_at<AT, 2, QMAX>(s.row[jj], it.a - 1);
       }
-#pragma unroll
-      for (int t = 0; t < QMAX; ++t)
-        if (t < q) xs[jj][t] = xq[t * s_x + ch];
-    }
-  }
-  AT gv[C::JG];
-  float gb[C::JG];
-#pragma unroll
-  for (int jj = 0; jj < C::JG; ++jj) {
-    const int j = tid + jj * C::NT;
-    const int t = j / D, k = j - t * D;
-    if (t < q) {
-      gv[jj] = graw[t * s_g + k];
-      gb[jj] = p.dt_bias[h * D + k];
-    }
-  }
-  AT bv{};
-  if (tid < q) bv = rbeta[tid * s_beta];
-  const float Ah = __expf(p.A_log[h]);
-
-  // ---- phase 0b: first half of the state tile into registers -------------
-  // (the second half is issued once the conv registers are free)
-  const int lg = tid % C::L;      // lane within its row group
-  const int rg = tid / C::L;      // row group
-  const float* __restrict__ sbase =
-      p.state + int64_t(it.slot) * p.s_slot + int64_t(h) * D * D;
-  constexpr int P0 = (C::PASSES + 1) / 2;
-  f4 st[C::PASSES][C::CHUNKS];
-#pragma unroll
-  for (int pp = 0; pp < P0; ++pp)
-#pragma unroll
-    for (int c = 0; c < C::CHUNKS; ++c)
-      st[pp][c] = ld_stream(sbase + (pp * C::RPP + rg) * D + c * 4 * C::L +
-                            4 * lg);
-
-  // ---- phase 0c: conv + SiLU, key record, roll ------------------------------
-#pragma unroll
-  for (int jj = 0; jj < C::JC; ++jj) {
-    const int j = tid + jj * C::NT;
-    if (j < 3 * D) {
-      const int part = j / D, d = j - part * D;
-      const int ch = part * HD + h * D + d;
-      float s0 = A::f(hist[jj][0]), s1 = A::f(hist[jj][1]),
-            s2 = A::f(hist[jj][2]);
+      float s0 = A::f(h0), s1 = A::f(h1), s2 = A::f(h2);
 #pragma unroll
       for (int t = 0; t < QMAX; ++t) {
         if (t < q) {
-          const float s3 = A::f(xs[jj][t]);
-          float acc = w[jj][0] * s0;
-          acc = fmaf(w[jj][1], s1, acc);
-          acc = fmaf(w[jj][2], s2, acc);
-          acc = fmaf(w[jj][3], s3, acc);
+          const float s3 = A::f(s.xs[jj][t]);
+          float acc = w[0] * s0;
+          acc = fmaf(w[1], s1, acc);
+          acc = fmaf(w[2], s2, acc);
+          acc = fmaf(w[3], s3, acc);
           const float yv = acc * sigmoidf_(acc);
           sm.y[part][t][d] = yv;
           if (part == 1 && rec_ok) {
@@ -262,31 +304,52 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
       // Roll: the two newest history entries, then the q new inputs, at
       // the front; positions past 2 + q keep their bytes.
       AT* csc = cs + ch * s_cc;
-      csc[0] = hist[jj][1];
-      csc[s_ct] = hist[jj][2];
+      if (row_fast) {
+        // the whole row in one pass; its tail is written back unchanged
+        constexpr int RE = QMAX + 2;
+        constexpr int EW = 4 / int(sizeof(AT));  // elements per dword
+        uint32_t nw[Small<D, QMAX, ACT_BF16>::RD];
 #pragma unroll
-      for (int t = 0; t < QMAX; ++t)
-        if (t < q) csc[(2 + t) * s_ct] = xs[jj][t];
+        for (int i = 0; i < Small<D, QMAX, ACT_BF16>::RD; ++i) nw[i] = 0;
+        [&]<int... E>(std::integer_sequence<int, E...>) {
+          auto put = [&](auto ec) {
+            constexpr int e = decltype(ec)::value;
+            AT v;
+            if constexpr (e == 0)
+              v = h1;
+            else if constexpr (e == 1)
+              v = h2;
+            else
+              v = (e - 2 < q) ? s.xs[jj][e - 2]
+                              : row_elem<AT, e>(s.row[jj]);
+            nw[e / EW] |= bits_of(v) << (32 / EW * (e % EW));
+          };
+          (put(std::integral_constant<int, E>{}), ...);
+        }(std::make_integer_sequence<int, RE>{});
+        uint32_t* wp = reinterpret_cast<uint32_t*>(csc);
+#pragma unroll
+        for (int i = 0; i < Small<D, QMAX, ACT_BF16>::RD; ++i) wp[i] = nw[i];
+      } else {
+        csc[0] = h1;
+        csc[s_ct] = h2;
+#pragma unroll
+        for (int t = 0; t < QMAX; ++t)
+          if (t < q) csc[(2 + t) * s_ct] = s.xs[jj][t];
+      }
     }
   }
 
-  // ---- second half of the state tile ---------------------------------------
-#pragma unroll
-  for (int pp = P0; pp < C::PASSES; ++pp)
-#pragma unroll
-    for (int c = 0; c < C::CHUNKS; ++c)
-      st[pp][c] = ld_stream(sbase + (pp * C::RPP + rg) * D + c * 4 * C::L +
-                            4 * lg);
+  mid();
 
-  // ---- phase 0d: gate decays, raw-gate record half, beta -------------------
   const bool use_lb = (p.flags & kLowerBound) != 0;
+  const float Ah = __expf(hr.alog);
 #pragma unroll
   for (int jj = 0; jj < C::JG; ++jj) {
     const int j = tid + jj * C::NT;
     const int t = j / D, k = j - t * D;
     if (t < q) {
-      const float g0 = A::f(gv[jj]);
-      sm.dec[t][k] = __expf(kda_gate(g0 + gb[jj], Ah, use_lb, p.lb));
+      const float g0 = A::f(s.gv[jj]);
+      sm.dec[t][k] = __expf(kda_gate(g0 + hr.gb[jj], Ah, use_lb, p.lb));
       if (rec_ok) {
         if (kg_bf16)
           kg16[t * s_kp + D + k] = f32_to_bf16(g0);
@@ -295,12 +358,23 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
       }
     }
   }
-  if (tid < q) sm.beta[tid] = sigmoidf_(A::f(bv));
-  if (tid == 0) sm.ticket[buf ^ 1] = drawn;
-  lds_barrier();
+  if (tid < q) sm.beta[tid] = sigmoidf_(A::f(s.bv));
+}
 
-  // Metadata of the next item: scalar loads in flight from here on.
-  advance();
+// Phases 1-4 of a live item (after the barrier that publishes phase 0),
+// with its state tile in registers.
+template <int D, int QMAX, bool FULL>
+__device__ __forceinline__ void item_back(const VerifyParams& p,
+                                          VerifySmem<D, QMAX>& sm,
+                                          const Item& it,
+                                          const Tile<D, QMAX>& st) {
+  using C = VerifyCfg<D, QMAX>;
+  const int tid = fresh_tid();
+  const int h = it.h;
+  const int q = FULL ? QMAX : it.q;
+  const bool rec_ok = it.rec_ok;
+  const int lg = tid % C::L;      // lane within its row group
+  const int rg = tid / C::L;      // row group
 
   // ---- phase 1: per-column partial sums, summed over columns in LDS ---------
   const int col = tid % D;
@@ -459,6 +533,106 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
   }
 }
 
+// Null block (null or out-of-pool slot): +0.0 outputs, no state, record or
+// conv byte touched.
+template <int D, int QMAX>
+__device__ __forceinline__ void null_item(const VerifyParams& p,
+                                          const Item& it) {
+  using C = VerifyCfg<D, QMAX>;
+  for (int j = fresh_tid(); j < it.q * D; j += C::NT) {
+    const int t = j / D, v = j - t * D;
+    st_elem(p.out, int64_t(it.bos + t) * p.s_out + int64_t(it.h) * D + v,
+            0.0f, (p.flags & kOutBf16) != 0);
+  }
+}
+
+// One live item, loads issued here (one-workgroup-per-item and ticket
+// schedules).  `drawn` is thread 0's freshly drawn ticket; it is published
+// through LDS at the first barrier, after which `advance()` starts the
+// scalar loads of the next item's metadata.
+template <int D, int QMAX, bool ACT_BF16, bool FULL, class Advance>
+__device__ __forceinline__ void verify_item(const VerifyParams& p,
+                                            VerifySmem<D, QMAX>& sm,
+                                            const Item& it, int drawn,
+                                            int buf, Advance&& advance) {
+  using C = VerifyCfg<D, QMAX>;
+  using AT = typename Act<ACT_BF16>::T;
+  const int tid = threadIdx.x;
+  const int h = it.h;
+  const int q = FULL ? QMAX : it.q;
+  const int HD = p.H * D;
+  // small loads first (vector-memory counters retire in issue order)
+  HeadRegs<D, QMAX> hr;
+  load_head<D, QMAX>(p, h, hr);
+  Small<D, QMAX, ACT_BF16> s;
+  {
+    const AT* __restrict__ xq =
+        static_cast<const AT*>(p.mixed_qkv) + int64_t(it.bos) * p.s_x;
+    const AT* __restrict__ cs =
+        static_cast<const AT*>(p.conv_state) + int64_t(it.slot) * p.s_cs_slot;
+    const AT* __restrict__ graw = static_cast<const AT*>(p.raw_gate) +
+                                  int64_t(it.bos) * p.s_g + h * D;
+    const AT* __restrict__ rbeta = static_cast<const AT*>(p.raw_beta) +
+                                   int64_t(it.bos) * p.s_beta + h;
+    const int s_cc = p.s_cs_chan, s_ct = p.s_cs_tok;
+#pragma unroll
+    for (int jj = 0; jj < C::JC; ++jj) {
+      const int j = tid + jj * C::NT;
+      if (j < 3 * D) {
+        const int part = j / D, d = j - part * D;
+        const int ch = part * HD + h * D + d;
+        if (p.flags & kConvRow) {
+          const uint32_t* rp = reinterpret_cast<const uint32_t*>(cs + ch * s_cc);
+#pragma unroll
+          for (int i = 0; i < Small<D, QMAX, ACT_BF16>::RD; ++i)
+            s.row[jj][i] = rp[i];
+        } else {
+          const int co = ch * s_cc + (it.a - 1) * s_ct;
+#pragma unroll
+          for (int i = 0; i < 3; ++i) s.hist[jj][i] = cs[co + i * s_ct];
+        }
+#pragma unroll
+        for (int t = 0; t < QMAX; ++t)
+          if (t < q) s.xs[jj][t] = xq[t * p.s_x + ch];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < C::JG; ++jj) {
+      const int j = tid + jj * C::NT;
+      const int t = j / D, k = j - t * D;
+      if (t < q) s.gv[jj] = graw[t * p.s_g + k];
+    }
+    s.bv = AT{};
+    if (tid < q) s.bv = rbeta[tid * p.s_beta];
+  }
+  // the state tile, in two halves (the second once the conv registers are
+  // free)
+  const int lg = tid % C::L, rg = tid / C::L;
+  const float* __restrict__ sbase =
+      p.state + int64_t(it.slot) * p.s_slot + int64_t(h) * D * D;
+  constexpr int P0 = (C::PASSES + 1) / 2;
+  Tile<D, QMAX> st;
+#pragma unroll
+  for (int pp = 0; pp < P0; ++pp)
+#pragma unroll
+    for (int c = 0; c < C::CHUNKS; ++c)
+      st[pp][c] = ld_stream(sbase + (pp * C::RPP + rg) * D + c * 4 * C::L +
+                            4 * lg);
+  item_front<D, QMAX, ACT_BF16, FULL>(p, sm, it, s, hr, [&] {
+#pragma unroll
+    for (int pp = P0; pp < C::PASSES; ++pp)
+#pragma unroll
+      for (int c = 0; c < C::CHUNKS; ++c)
+        st[pp][c] = ld_stream(sbase + (pp * C::RPP + rg) * D +
+                              c * 4 * C::L + 4 * lg);
+  });
+  if (tid == 0) sm.ticket[buf ^ 1] = drawn;
+  lds_barrier();
+  // Metadata of the next item: scalar loads in flight from here on.
+  advance();
+  item_back<D, QMAX, FULL>(p, sm, it, st);
+}
+
 template <int D, int QMAX, bool ACT_BF16>
 __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
                                   (VerifyCfg<D, QMAX>::MIN_WAVES))
@@ -549,29 +723,46 @@ __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
   }
 }
 
-// grid <= 0: one workgroup per item (the default).  grid > 0: a persistent
-// grid of at most `grid` workgroups drawing tickets from p.counter (also
-// used when the batch exceeds the 65535 requests a grid row can address).
+// Workgroups of `kern` resident on the current device at once (cached per
+// device: the value does not change during the process).
+template <class K>
+int resident_grid(K kern, int threads, int* cache, int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return 0;
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(kern), threads, 0);
+  if (e != hipSuccess) return int(e);
+  *out = max(1, cus * max(per_cu, 1));
+  if (dev >= 0 && dev < 64) cache[dev] = *out;
+  return 0;
+}
+
 template <int D, int QMAX, bool ACT_BF16>
-int launch_one(const VerifyParams& p, int grid, hipStream_t stream) {
+int launch_one(const VerifyParams& p, int schedule, int grid,
+               hipStream_t stream) {
   using C = VerifyCfg<D, QMAX>;
-  if (grid <= 0 && p.B <= 65535) {
+  // One workgroup per item is the default: on gfx950 the hardware
+  // dispatcher balances ragged windows by itself and the per-item kernel
+  // carries no loop state, which the ticket loop pays for in registers.
+  if (schedule != kScheduleTickets && p.B <= 65535) {
     hipLaunchKernelGGL((kda_verify_grid_kernel<D, QMAX, ACT_BF16>),
                        dim3(p.H, p.B), dim3(C::NT), 0, stream, p);
     return int(hipGetLastError());
   }
+  // Tickets (also for more requests than a grid row holds).
   auto kern = kda_verify_kernel<D, QMAX, ACT_BF16>;
   if (grid <= 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess)
-      e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
-                                dev);
-    if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(kern), C::NT, 0);
-    if (e != hipSuccess) return int(e);
-    grid = max(1, cus * max(per_cu, 1));
+    static int cache[64];
+    const int e = resident_grid(kern, C::NT, cache, &grid);
+    if (e != 0) return e;
   }
   if (p.counter == nullptr) return int(hipErrorInvalidValue);
   VerifyParams q = p;
@@ -583,19 +774,20 @@ int launch_one(const VerifyParams& p, int grid, hipStream_t stream) {
 }
 
 template <int D, bool ACT_BF16>
-int launch_q(const VerifyParams& p, int grid, hipStream_t stream) {
-  if (p.Q <= 4) return launch_one<D, 4, ACT_BF16>(p, grid, stream);
-  if (p.Q <= 8) return launch_one<D, 8, ACT_BF16>(p, grid, stream);
-  return launch_one<D, 16, ACT_BF16>(p, grid, stream);
+int launch_q(const VerifyParams& p, int sched, int grid, hipStream_t stream) {
+  if (p.Q <= 4) return launch_one<D, 4, ACT_BF16>(p, sched, grid, stream);
+  if (p.Q <= 8) return launch_one<D, 8, ACT_BF16>(p, sched, grid, stream);
+  return launch_one<D, 16, ACT_BF16>(p, sched, grid, stream);
 }
 
 template <bool ACT_BF16>
-int launch_d(const VerifyParams& p, int D, int grid, hipStream_t stream) {
+int launch_d(const VerifyParams& p, int D, int sched, int grid,
+             hipStream_t stream) {
   switch (D) {
-    case 16: return launch_q<16, ACT_BF16>(p, grid, stream);
-    case 32: return launch_q<32, ACT_BF16>(p, grid, stream);
-    case 64: return launch_q<64, ACT_BF16>(p, grid, stream);
-    case 128: return launch_q<128, ACT_BF16>(p, grid, stream);
+    case 16: return launch_q<16, ACT_BF16>(p, sched, grid, stream);
+    case 32: return launch_q<32, ACT_BF16>(p, sched, grid, stream);
+    case 64: return launch_q<64, ACT_BF16>(p, sched, grid, stream);
+    case 128: return launch_q<128, ACT_BF16>(p, sched, grid, stream);
     default: return int(hipErrorInvalidValue);
   }
 }
@@ -606,10 +798,10 @@ __global__ void kda_reset_kernel(int32_t* counter, int n) {
 
 }  // namespace
 
-int launch_verify(const VerifyParams& p, int D, bool act_bf16, int grid,
-                  hipStream_t stream) {
-  return act_bf16 ? launch_d<true>(p, D, grid, stream)
-                  : launch_d<false>(p, D, grid, stream);
+int launch_verify(const VerifyParams& p, int D, bool act_bf16, int schedule,
+                  int grid, hipStream_t stream) {
+  return act_bf16 ? launch_d<true>(p, D, schedule, grid, stream)
+                  : launch_d<false>(p, D, schedule, grid, stream);
 }
 
 int launch_reset_counter(int32_t* counter, int n, hipStream_t stream) {

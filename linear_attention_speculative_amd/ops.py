@@ -83,7 +83,8 @@ def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
                 conv_weight, query_start_loc, state_indices,
                 num_accepted_tokens, spec_query_len, conv_dim_first,
                 work_counter, record_rows=None, null_block_id=0,
-                max_workgroups=0, items_per_ticket=0) -> _abi.KdaVerifyArgs:
+                max_workgroups=0, items_per_ticket=0,
+                schedule=0) -> _abi.KdaVerifyArgs:
     a = _abi.KdaVerifyArgs()
     a.mixed_qkv = describe(mixed_qkv)
     a.raw_gate = describe(raw_gate)
@@ -109,6 +110,7 @@ def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
     a.lower_bound = 0.0 if lower_bound is None else float(lower_bound)
     a.max_workgroups = max_workgroups
     a.items_per_ticket = items_per_ticket
+    a.schedule = schedule
     return a
 
 

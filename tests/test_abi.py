@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_abi.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert kda.abi_version() == 1
+    assert kda.abi_version() == 2
     assert lib.kda_status_string(_abi.KDA_E_UNALIGNED) == b"KDA_E_UNALIGNED"
 
 
@@ -156,11 +156,18 @@ def test_capacity_and_argument_errors():
     assert _code(kw) == _abi.KDA_E_CAPACITY
     wl, kw = _kw()
     kw["work_counter"] = None
-    assert _code(kw) == 0            # the default schedule has no counter
-    kw["max_workgroups"] = 8
+    for sched in (_abi.KDA_SCHEDULE_DEFAULT, _abi.KDA_SCHEDULE_PER_ITEM):
+        kw["schedule"] = sched       # no counter needed
+        assert _code(kw) == 0
+    kw["schedule"] = _abi.KDA_SCHEDULE_TICKETS
     assert _code(kw) == _abi.KDA_E_ARG
-    kw["max_workgroups"] = -1        # negative: default schedule
-    assert _code(kw) == 0
+    for bad in (-1, 3):
+        kw["schedule"] = bad
+        assert _code(kw) == _abi.KDA_E_ARG
+    kw["schedule"] = 0
+    kw["max_workgroups"] = -1
+    assert _code(kw) == _abi.KDA_E_ARG
+    kw["max_workgroups"] = 0
     kw["items_per_ticket"] = -2
     assert _code(kw) == _abi.KDA_E_ARG
 

@@ -59,14 +59,14 @@ def _check_pages(wl, layer, page_before, rec_before=None):
         assert torch.equal(L.record_page[keep], rec_before[keep])
 
 
-def _verify_case(wl, layer=0, reqs=None, max_wg=0, kg_tol=None):
+def _verify_case(wl, layer=0, reqs=None, max_wg=0, kg_tol=None, sched=0):
     L = wl.layers[layer]
     sample = snapshot(wl, layer, reqs)
     state_before = L.state.clone()
     page_before = L.page.clone()
     rec_before = None if L.record_page is None else L.record_page.clone()
     counter = _counter()
-    drive.verify(wl, layer, counter, max_workgroups=max_wg)
+    drive.verify(wl, layer, counter, max_workgroups=max_wg, schedule=sched)
     torch.cuda.synchronize()
     assert int(counter.item()) == 0, "ticket counter must be left at 0"
     assert torch.equal(L.state, state_before), "verify wrote the checkpoint"
@@ -162,7 +162,9 @@ def test_sweep_head_dim_and_window(D, Q, act):
                        weight=act, null_frac=0.15,
                        conv_dim_first=(D + Q) % 2 == 0,
                        gates=[-5.0 if Q % 2 else None], act_row_pad=8)
-    sample, ref, errs = _verify_case(wl)
+    # each schedule (per item, tickets) sees half of the shapes
+    sched = (1, 2)[(D + Q + len(act)) % 2]
+    sample, ref, errs = _verify_case(wl, sched=sched)
     _commit_case(wl, {0: (sample, ref)})
 
 
@@ -260,10 +262,13 @@ def test_results_independent_of_grid_size():
     L = wl.layers[0]
     page0, rec0 = L.page.clone(), None
     outs = []
-    for grid, per in ((1, 0), (3, 0), (0, 0), (0, 3), (5, 7), (2, 1000)):
+    # (schedule, max_workgroups, items_per_ticket)
+    for sched, grid, per in ((0, 0, 0), (1, 0, 0), (2, 1, 0), (2, 3, 0),
+                             (2, 0, 3), (2, 5, 7), (2, 2, 1000)):
         L.page.copy_(page0)
         c = _counter()
-        drive.verify(wl, 0, c, max_workgroups=grid, items_per_ticket=per)
+        drive.verify(wl, 0, c, max_workgroups=grid, items_per_ticket=per,
+                     schedule=sched)
         torch.cuda.synchronize()
         assert int(c.item()) == 0
         outs.append((L.out.clone(), L.page.clone()))
@@ -276,7 +281,7 @@ def test_counter_protocol_and_reset():
     wl = make_workload("ragged", DEV, B=8, H=2, D=16, Q=4, N=12)
     c = _counter()
     for _ in range(3):
-        drive.verify(wl, 0, c, max_workgroups=5)
+        drive.verify(wl, 0, c, max_workgroups=5, schedule=2)
         torch.cuda.synchronize()
         assert int(c.item()) == 0
     c.fill_(123)
