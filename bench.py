@@ -13,10 +13,14 @@ commit walk the requests in the same order, so each state tile returns from
 HBM).
 
 Prints one JSON line.  `value` is verified tokens per second (draft tokens
-verified per step / step time); `roofline` describes the kernel that takes
-the most time per step, from HIP events around its launches;
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
-workload.
+verified per step / step time over K back-to-back steps); `roofline`
+describes the kernel that takes the most time per step, from HIP events
+around its launches; `kernels` gives each kernel's median, p10 and p90 over
+the timed steps, the median of single synchronized launches, and the
+median of single launches that each follow an untimed 1 GiB write (which
+evicts the caches), so that any help from the last-level cache between
+kernels shows up as a difference; `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
   python bench.py --copy-calibration   # plain copy for HBM counter scaling
@@ -168,6 +172,8 @@ def main() -> int:
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cold", type=int, default=10,
+                    help="launches timed after a cache-evicting write")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -215,11 +221,57 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    v_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    c_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    v_all = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in events)
+    c_all = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in events)
+    v_ms = sum(v_all) / args.steps / 1e3
+    c_ms = sum(c_all) / args.steps / 1e3
     print(f"# timed {args.steps} steps: {ms_step:.4f} ms/step (verify "
           f"{v_ms * 1e3:.1f} us, commit {c_ms * 1e3:.1f} us)",
           file=sys.stderr, flush=True)
+
+    def quant(xs, q):
+        return xs[min(len(xs) - 1, int(q * len(xs)))]
+
+    # Cold launches: each after an untimed 1 GiB write.
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cold_v, cold_c = [], []
+    for k in range(args.cold):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        scratch.fill_(float(k))
+        ev[0].record()
+        drive.verify(wl, 0, counter)
+        ev[1].record()
+        scratch.fill_(float(k) + 0.5)
+        ev[2].record()
+        ctx.commit(wl.state_indices, wl.commit_lens,
+                   record_rows=wl.record_rows)
+        ev[3].record()
+        torch.cuda.synchronize()
+        cold_v.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        cold_c.append(ev[2].elapsed_time(ev[3]) * 1e3)
+    del scratch
+    cold_v.sort()
+    cold_c.sort()
+    # The same single launches without the evicting write: the difference
+    # to the back-to-back steps is launch ramp-up and drain, the difference
+    # to the cold launches is what the caches kept between kernels.
+    iso_v, iso_c = [], []
+    for k in range(args.cold):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        drive.verify(wl, 0, counter)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ev[2].record()
+        ctx.commit(wl.state_indices, wl.commit_lens,
+                   record_rows=wl.record_rows)
+        ev[3].record()
+        torch.cuda.synchronize()
+        iso_v.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        iso_c.append(ev[2].elapsed_time(ev[3]) * 1e3)
+    iso_v.sort()
+    iso_c.sort()
 
     tokens = nbytes["tokens"]
     kernels = {
@@ -263,6 +315,14 @@ def main() -> int:
                      "verify_us": v_ms * 1e3, "commit_us": c_ms * 1e3,
                      "verify_GB/s": nbytes["verify"] / (v_ms * 1e-3) / 1e9,
                      "commit_GB/s": nbytes["commit"] / (c_ms * 1e-3) / 1e9},
+        "kernels": {
+            name: {"median_us": quant(xs, 0.5), "p10_us": quant(xs, 0.1),
+                   "p90_us": quant(xs, 0.9),
+                   "single_launch_median_us": quant(si, 0.5) if si else None,
+                   "cold_median_us": quant(cs, 0.5) if cs else None}
+            for name, xs, si, cs in (
+                ("kda_verify_grid_kernel", v_all, iso_v, cold_v),
+                ("kda_commit_grid_kernel", c_all, iso_c, cold_c))},
     }
     if args.cpu_seconds > 0:
         print("# cpu baseline ...", file=sys.stderr, flush=True)
