@@ -153,6 +153,17 @@ typedef struct {
   int32_t items_per_ticket; /* ticket schedule: (request, head) items
                                claimed per ticket; 0 = library default */
   int32_t schedule;        /* kda_schedule */
+  const int32_t* pending_lens; /* device [batch] or NULL.  When given, the
+                              launch first performs the deferred commit of
+                              the previous step (state page, deferred
+                              commit; ops page `_commit_kda_state_kernel`):
+                              the first pending_lens[b] positions (clamped
+                              to [0, Q]) recorded in request b's record row
+                              are folded into its checkpoint, which is
+                              written back in place, and the verify then
+                              starts from the updated state and overwrites
+                              that row with this step's records.  Uses the
+                              per-item schedule (batch <= 65535). */
 } kda_verify_args;
 
 /* Arguments of kda_recoverssm_commit.  Per-layer tensors are described by

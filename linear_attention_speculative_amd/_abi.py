@@ -55,6 +55,7 @@ class KdaVerifyArgs(Structure):
         ("use_lower_bound", c_int32), ("lower_bound", c_float),
         ("max_workgroups", c_int32), ("items_per_ticket", c_int32),
         ("schedule", c_int32),
+        ("pending_lens", c_void_p),
     ]
 
 

@@ -272,9 +272,13 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
                   "are required");
     if (!a->work_counter && a->schedule == KDA_SCHEDULE_TICKETS)
       return fail(KDA_E_ARG, "the ticket schedule needs a work_counter");
+    if (a->pending_lens && a->batch > 65535)
+      return fail(KDA_E_UNSUPPORTED,
+                  "the deferred flush runs one workgroup per item and "
+                  "supports at most 65535 requests");
     const void* ptrs[] = {a->query_start_loc, a->state_indices,
                           a->num_accepted_tokens, a->record_rows,
-                          a->work_counter};
+                          a->work_counter, a->pending_lens};
     for (const void* q : ptrs)
       if (q && !aligned(q, 4))
         return fail(KDA_E_UNALIGNED, "metadata pointers must be 4-byte "
@@ -334,6 +338,7 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
   p.slots = a->state_indices;
   p.accepted = a->num_accepted_tokens;
   p.record_rows = a->record_rows;
+  p.pending = a->pending_lens;
   p.counter = a->work_counter;
   p.B = a->batch;
   p.H = int32_t(H);

@@ -29,6 +29,7 @@ struct VerifyParams {
   const int32_t* slots;
   const int32_t* accepted;
   const int32_t* record_rows;  // may be null
+  const int32_t* pending;      // may be null: positions to flush first
   int32_t* counter;
   int32_t s_x, s_g, s_beta, s_slot;
   int32_t s_c_row, s_c_head, s_c_pos;

@@ -97,6 +97,20 @@ struct alignas(16) VerifySmem {
   int ticket[2];
 };
 
+// LDS of the deferred flush (fused commit of the previous step's pending
+// positions before the verify): per column the decay product Gam and the
+// vectors k_hat_t * Suf_t, per row the pending corrections.
+template <int D, int QMAX, bool FLUSH>
+struct alignas(16) FlushSmem {
+  float gam[D];               // Gam = prod_{t<n} d_t
+  float w[QMAX][D];           // raw keys, then k_hat_t * Suf_t
+  float dec[QMAX][D];         // pending decays d_t
+  float cT[D][QMAX + 1];      // corrections, row v: c_0 .. c_{n-1}
+  float ksum[QMAX];           // |k_t|^2
+};
+template <int D, int QMAX>
+struct FlushSmem<D, QMAX, false> {};
+
 // Index of the pair terms in the reduction vector.
 template <int QMAX>
 __device__ __forceinline__ constexpr int idx_m(int t, int s) {
@@ -363,11 +377,11 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
 
 // Phases 1-4 of a live item (after the barrier that publishes phase 0),
 // with its state tile in registers.
-template <int D, int QMAX, bool FULL>
+template <int D, int QMAX, bool FULL, class PreDots>
 __device__ __forceinline__ void item_back(const VerifyParams& p,
                                           VerifySmem<D, QMAX>& sm,
-                                          const Item& it,
-                                          const Tile<D, QMAX>& st) {
+                                          const Item& it, Tile<D, QMAX>& st,
+                                          PreDots&& pre_dots) {
   using C = VerifyCfg<D, QMAX>;
   const int tid = fresh_tid();
   const int h = it.h;
@@ -457,6 +471,9 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
   }
   lds_barrier();
 
+  // (the deferred flush folds the pending positions into the tile here)
+  pre_dots(st);
+
   // ---- phase 3: 2q dot products per state row ---------------------------------
   // Position-outer order: each position's two column vectors are read from
   // LDS once and applied to every pass of the register-resident tile; the
@@ -533,6 +550,142 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
   }
 }
 
+// ---- deferred flush ----------------------------------------------------------
+// The previous step's records of this item's record row hold n pending
+// positions; the fused kernel folds them into the checkpoint (ops page
+// `_commit_kda_state_kernel`, applied in place) before verifying, so the
+// state tile is read once and written once for commit and verify together
+// (state page, deferred commit).
+
+// Raw pending record values: position t = j / D, element j % D.
+template <int D, int QMAX>
+struct PendingRegs {
+  using C = VerifyCfg<D, QMAX>;
+  float cv[C::JG];     // correction c_t[v]
+  uint32_t kr[C::JG];  // raw key k_t[k] (f32 bits, or a bf16 in the low half)
+  uint32_t gr[C::JG];  // raw gate
+};
+
+template <int D, int QMAX>
+__device__ __forceinline__ void load_pending(const VerifyParams& p,
+                                             const Item& it, int n,
+                                             PendingRegs<D, QMAX>& pr) {
+  using C = VerifyCfg<D, QMAX>;
+  const int tid = fresh_tid();
+  const bool kg_bf16 = (p.flags & kKgBf16) != 0;
+  const float* corr = p.correction + int64_t(it.r) * p.s_c_row +
+                      int64_t(it.h) * p.s_c_head;
+  const int64_t kg_off =
+      int64_t(it.r) * p.s_kg_row + int64_t(it.h) * p.s_kg_head;
+#pragma unroll
+  for (int jj = 0; jj < C::JG; ++jj) {
+    const int j = tid + jj * C::NT;
+    const int t = j / D, k = j % D;
+    pr.cv[jj] = 0.0f;
+    pr.kr[jj] = 0;
+    pr.gr[jj] = 0;
+    if (t < n) {
+      pr.cv[jj] = corr[t * p.s_c_pos + k];
+      const int64_t o = kg_off + int64_t(t) * p.s_kg_pos + k;
+      if (kg_bf16) {
+        pr.kr[jj] = static_cast<const uint16_t*>(p.key_gate)[o];
+        pr.gr[jj] = static_cast<const uint16_t*>(p.key_gate)[o + D];
+      } else {
+        pr.kr[jj] = static_cast<const uint32_t*>(p.key_gate)[o];
+        pr.gr[jj] = static_cast<const uint32_t*>(p.key_gate)[o + D];
+      }
+    }
+  }
+}
+
+// Per column: Gam = prod_{t<n} d_t and w_t = k_hat_t * prod_{t<s<n} d_s;
+// per row: the corrections.  Ends with a barrier.
+template <int D, int QMAX>
+__device__ __forceinline__ void flush_prepare(const VerifyParams& p,
+                                              FlushSmem<D, QMAX, true>& fs,
+                                              int n,
+                                              const PendingRegs<D, QMAX>& pr,
+                                              const HeadRegs<D, QMAX>& hr) {
+  using C = VerifyCfg<D, QMAX>;
+  const int tid = fresh_tid();
+  const int lane = tid % 64, wave = tid / 64;
+  const bool kg_bf16 = (p.flags & kKgBf16) != 0;
+  const bool use_lb = (p.flags & kLowerBound) != 0;
+  const float Ah = __expf(hr.alog);
+  auto f = [&](uint32_t raw) {
+    return __uint_as_float(kg_bf16 ? raw << 16 : raw);
+  };
+#pragma unroll
+  for (int jj = 0; jj < C::JG; ++jj) {
+    const int j = tid + jj * C::NT;
+    const int t = j / D, k = j % D;
+    if (t < QMAX) {
+      const bool ok = t < n;
+      fs.cT[k][t] = pr.cv[jj];
+      fs.w[t][k] = ok ? f(pr.kr[jj]) : 0.0f;
+      fs.dec[t][k] =
+          ok ? __expf(kda_gate(f(pr.gr[jj]) + hr.gb[jj], Ah, use_lb, p.lb))
+             : 1.0f;
+    }
+  }
+  lds_barrier();
+  for (int t = wave; t < QMAX; t += C::NT / 64) {
+    float x = 0.0f;
+    for (int c = lane; c < D; c += 64) x += fs.w[t][c] * fs.w[t][c];
+    const float tot = wave_sum(x);
+    if (lane == 0) fs.ksum[t] = tot;
+  }
+  lds_barrier();
+  if (tid < D) {
+    float suf = 1.0f;
+#pragma unroll
+    for (int t = QMAX - 1; t >= 0; --t) {
+      if (t < n) {
+        fs.w[t][tid] *= rsqrtf(fs.ksum[t] + kNormEps) * suf;
+        suf *= fs.dec[t][tid];
+      }
+    }
+    fs.gam[tid] = suf;
+  }
+  lds_barrier();
+}
+
+// S <- S diag(Gam) + sum_{t<n} c_t w_t^T on the register tile, written back
+// to the checkpoint slot.
+template <int D, int QMAX>
+__device__ __forceinline__ void flush_fold(const VerifyParams& p,
+                                           const FlushSmem<D, QMAX, true>& fs,
+                                           const Item& it, int n,
+                                           Tile<D, QMAX>& st) {
+  using C = VerifyCfg<D, QMAX>;
+  const int tid = fresh_tid();
+  const int lg = tid % C::L, rg = tid / C::L;
+  float* dst = const_cast<float*>(p.state) + int64_t(it.slot) * p.s_slot +
+               int64_t(it.h) * D * D;
+#pragma unroll
+  for (int pp = 0; pp < C::PASSES; ++pp) {
+    const int row = pp * C::RPP + rg;
+#pragma unroll
+    for (int c = 0; c < C::CHUNKS; ++c) {
+      const int col = c * 4 * C::L + 4 * lg;
+      f4 acc = st[pp][c] * *reinterpret_cast<const f4*>(&fs.gam[col]);
+#pragma unroll
+      for (int t = 0; t < QMAX; ++t) {
+        if (t < n) {
+          const float cv = fs.cT[row][t];
+          const f4 w4 = *reinterpret_cast<const f4*>(&fs.w[t][col]);
+          acc.x = fmaf(cv, w4.x, acc.x);
+          acc.y = fmaf(cv, w4.y, acc.y);
+          acc.z = fmaf(cv, w4.z, acc.z);
+          acc.w = fmaf(cv, w4.w, acc.w);
+        }
+      }
+      st[pp][c] = acc;
+      st_stream(dst + row * D + col, acc);
+    }
+  }
+}
+
 // Null block (null or out-of-pool slot): +0.0 outputs, no state, record or
 // conv byte touched.
 template <int D, int QMAX>
@@ -550,9 +703,11 @@ __device__ __forceinline__ void null_item(const VerifyParams& p,
 // schedules).  `drawn` is thread 0's freshly drawn ticket; it is published
 // through LDS at the first barrier, after which `advance()` starts the
 // scalar loads of the next item's metadata.
-template <int D, int QMAX, bool ACT_BF16, bool FULL, class Advance>
+template <int D, int QMAX, bool ACT_BF16, bool FULL, bool FLUSH,
+          class Advance>
 __device__ __forceinline__ void verify_item(const VerifyParams& p,
                                             VerifySmem<D, QMAX>& sm,
+                                            FlushSmem<D, QMAX, FLUSH>& fs,
                                             const Item& it, int drawn,
                                             int buf, Advance&& advance) {
   using C = VerifyCfg<D, QMAX>;
@@ -564,6 +719,13 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
   // small loads first (vector-memory counters retire in issue order)
   HeadRegs<D, QMAX> hr;
   load_head<D, QMAX>(p, h, hr);
+  // deferred flush: positions still pending in the record row
+  int n_pend = 0;
+  PendingRegs<D, QMAX> pr;
+  if constexpr (FLUSH) {
+    if (it.rec_ok) n_pend = min(max(sload1(p.pending + it.b), 0), p.Q);
+    if (n_pend > 0) load_pending<D, QMAX>(p, it, n_pend, pr);
+  }
   Small<D, QMAX, ACT_BF16> s;
   {
     const AT* __restrict__ xq =
@@ -618,6 +780,11 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
     for (int c = 0; c < C::CHUNKS; ++c)
       st[pp][c] = ld_stream(sbase + (pp * C::RPP + rg) * D + c * 4 * C::L +
                             4 * lg);
+  // the pending records are read (and their LDS views built) before phase
+  // 0 writes this step's records into the same row
+  if constexpr (FLUSH) {
+    if (n_pend > 0) flush_prepare<D, QMAX>(p, fs, n_pend, pr, hr);
+  }
   item_front<D, QMAX, ACT_BF16, FULL>(p, sm, it, s, hr, [&] {
 #pragma unroll
     for (int pp = P0; pp < C::PASSES; ++pp)
@@ -630,7 +797,11 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
   lds_barrier();
   // Metadata of the next item: scalar loads in flight from here on.
   advance();
-  item_back<D, QMAX, FULL>(p, sm, it, st);
+  item_back<D, QMAX, FULL>(p, sm, it, st, [&](Tile<D, QMAX>& t) {
+    if constexpr (FLUSH) {
+      if (n_pend > 0) flush_fold<D, QMAX>(p, fs, it, n_pend, t);
+    }
+  });
 }
 
 template <int D, int QMAX, bool ACT_BF16>
@@ -639,6 +810,7 @@ __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
     kda_verify_kernel(VerifyParams p) {
   using C = VerifyCfg<D, QMAX>;
   __shared__ VerifySmem<D, QMAX> sm;
+  FlushSmem<D, QMAX, false> nofs;
   const int tid = threadIdx.x;
   // Ticket protocol: a ticket claims per_ticket consecutive items.  Every
   // workgroup draws tickets until one is past the last, drawing the next
@@ -671,9 +843,11 @@ __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
     };
     if (it.live) {
       if (it.q == QMAX)
-        verify_item<D, QMAX, ACT_BF16, true>(p, sm, it, drawn, buf, advance);
+        verify_item<D, QMAX, ACT_BF16, true, false>(p, sm, nofs, it, drawn,
+                                                    buf, advance);
       else
-        verify_item<D, QMAX, ACT_BF16, false>(p, sm, it, drawn, buf,
+        verify_item<D, QMAX, ACT_BF16, false, false>(p, sm, nofs, it, drawn,
+                                                     buf,
                                               advance);
     } else {
       // Null block: zero outputs, touch no state, record or conv byte.
@@ -700,19 +874,23 @@ __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
 // request, so the hardware dispatcher hands out items in request-major
 // order and refills each compute unit as workgroups retire (which also
 // balances ragged windows).  No loop-carried state, no ticket counter.
-template <int D, int QMAX, bool ACT_BF16>
+// FLUSH: the deferred flush of pending record positions comes first.
+template <int D, int QMAX, bool ACT_BF16, bool FLUSH>
 __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
                                   (VerifyCfg<D, QMAX>::MIN_WAVES))
     kda_verify_grid_kernel(VerifyParams p) {
   using C = VerifyCfg<D, QMAX>;
   __shared__ VerifySmem<D, QMAX> sm;
+  __shared__ FlushSmem<D, QMAX, FLUSH> fs;
   const Item it = load_item(p, int(blockIdx.y), int(blockIdx.x));
   auto advance = [] {};
   if (it.live) {
     if (it.q == QMAX)
-      verify_item<D, QMAX, ACT_BF16, true>(p, sm, it, 0, 0, advance);
+      verify_item<D, QMAX, ACT_BF16, true, FLUSH>(p, sm, fs, it, 0, 0,
+                                                  advance);
     else
-      verify_item<D, QMAX, ACT_BF16, false>(p, sm, it, 0, 0, advance);
+      verify_item<D, QMAX, ACT_BF16, false, FLUSH>(p, sm, fs, it, 0, 0,
+                                                   advance);
   } else {
     // Null block: zero outputs, touch no state, record or conv byte.
     for (int j = threadIdx.x; j < it.q * D; j += C::NT) {
@@ -752,8 +930,14 @@ int launch_one(const VerifyParams& p, int schedule, int grid,
   // One workgroup per item is the default: on gfx950 the hardware
   // dispatcher balances ragged windows by itself and the per-item kernel
   // carries no loop state, which the ticket loop pays for in registers.
+  if (p.pending != nullptr) {  // the deferred flush: per-item kernel only
+    if (p.B > 65535) return int(hipErrorInvalidConfiguration);
+    hipLaunchKernelGGL((kda_verify_grid_kernel<D, QMAX, ACT_BF16, true>),
+                       dim3(p.H, p.B), dim3(C::NT), 0, stream, p);
+    return int(hipGetLastError());
+  }
   if (schedule != kScheduleTickets && p.B <= 65535) {
-    hipLaunchKernelGGL((kda_verify_grid_kernel<D, QMAX, ACT_BF16>),
+    hipLaunchKernelGGL((kda_verify_grid_kernel<D, QMAX, ACT_BF16, false>),
                        dim3(p.H, p.B), dim3(C::NT), 0, stream, p);
     return int(hipGetLastError());
   }

@@ -84,7 +84,7 @@ def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
                 num_accepted_tokens, spec_query_len, conv_dim_first,
                 work_counter, record_rows=None, null_block_id=0,
                 max_workgroups=0, items_per_ticket=0,
-                schedule=0) -> _abi.KdaVerifyArgs:
+                schedule=0, pending_lens=None) -> _abi.KdaVerifyArgs:
     a = _abi.KdaVerifyArgs()
     a.mixed_qkv = describe(mixed_qkv)
     a.raw_gate = describe(raw_gate)
@@ -111,6 +111,7 @@ def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
     a.max_workgroups = max_workgroups
     a.items_per_ticket = items_per_ticket
     a.schedule = schedule
+    a.pending_lens = _ptr(pending_lens)
     return a
 
 
@@ -123,7 +124,9 @@ def check_verify(**kwargs) -> int:
 def conv_update_verify(*, stream=None, **kwargs) -> None:
     """Fused conv update + speculative verify of one KDA layer on the current
     (or given) stream.  Arguments follow kda_verify_args in
-    include/kda_recoverssm.h; `lower_bound=None` selects the softplus gate.
+    include/kda_recoverssm.h; `lower_bound=None` selects the softplus gate;
+    `pending_lens` (int32 [batch]) first folds the previous step's pending
+    record positions into the checkpoints (the deferred commit).
     Raises KdaUnaligned (nothing launched) for misaligned activations and
     KdaError for any other rejected argument."""
     a = verify_args(**kwargs)

@@ -383,6 +383,75 @@ def test_deferred_sequence_sampled():
         print("deferred", layer, errs)
 
 
+def _flush_case(wl, reqs=None, layers=(0,)):
+    """Previous step: verify (records); this step: the fused launch that
+    folds the pending positions (wl.commit_lens) and verifies.  Oracle:
+    commit, then verify from the committed state, rolled conv state and the
+    previous records."""
+    first = {}
+    for layer in layers:
+        first[layer] = snapshot(wl, layer, reqs)
+        drive.verify(wl, layer, _counter())
+    torch.cuda.synchronize()
+    pending = wl.commit_lens.cpu().numpy()
+    out = {}
+    for layer in layers:
+        L = wl.layers[layer]
+        s0 = first[layer]
+        r0 = run_oracle_verify(s0)
+        (new, written), = oracle.commit(
+            layers=[commit_layer_inputs(s0, r0, L)],
+            state_indices=s0.new_slot, commit_lens=pending[s0.reqs],
+            spec_query_len=wl.Q, record_rows=s0.new_row)
+        inp = dict(s0.inputs)
+        inp["state"] = new
+        inp["conv_state"] = r0["conv_state"]
+        inp["correction"] = r0["correction"]
+        inp["key_gate"] = r0["key_gate"]
+        s1 = snapshot(wl, layer, reqs)
+        ref1 = oracle.conv_update_verify(**inp)
+        state_before = L.state.clone()
+        drive.verify(wl, layer, _counter(), pending_lens=wl.commit_lens)
+        torch.cuda.synchronize()
+        cerr = check_commit(wl, layer, s0, new, written)
+        errs = check_verify(wl, layer, s1, ref1)
+        # slots with nothing pending (or null, or no record row) keep their
+        # checkpoint bit for bit
+        slots = wl.state_indices.cpu().numpy()
+        rows = (slots if wl.record_rows is None
+                else wl.record_rows.cpu().numpy())
+        for b in range(wl.B):
+            sl = int(slots[b])
+            if 0 < sl < wl.N and (pending[b] <= 0 or not 0 <= rows[b] < wl.R):
+                assert torch.equal(bits_t(L.state[sl]), bits_t(state_before[sl]))
+        out[layer] = (cerr, errs)
+    return out
+
+
+def bits_t(t):
+    return t.contiguous().view(torch.int32)
+
+
+@pytest.mark.parametrize("D,Q,act", [(128, 4, "bf16"), (64, 8, "f32"),
+                                     (32, 3, "bf16"), (16, 16, "f32")])
+def test_deferred_flush_fused(D, Q, act):
+    wl = make_workload("ragged", DEV, B=20, H=3, D=D, Q=Q, N=32, act=act,
+                       weight=act, null_frac=0.15,
+                       conv_dim_first=Q % 2 == 0)
+    # pending positions: at most what the previous verify recorded, some 0
+    rng = np.random.default_rng(D + Q)
+    qlen = (wl.query_start_loc[1:] - wl.query_start_loc[:-1]).cpu().numpy()
+    pend = np.minimum(rng.integers(0, Q + 1, size=wl.B), qlen)
+    wl.commit_lens.copy_(torch.tensor(pend, dtype=torch.int32))
+    print("flush", D, Q, act, _flush_case(wl))
+
+
+def test_deferred_flush_fused_sampled():
+    wl = make_workload("deferred", DEV)
+    print("flush deferred", _flush_case(wl, list(range(0, wl.B, 32)),
+                                        layers=(0, 1)))
+
+
 def test_commit_schedules_agree_bitwise():
     # The persistent strided schedule and the one-workgroup-per-item grid
     # compute every item with the same code: identical bytes.

@@ -17,7 +17,7 @@ from .gen import Workload
 
 def verify_kwargs(wl: Workload, layer: int, counter: torch.Tensor,
                   max_workgroups: int = 0, items_per_ticket: int = 0,
-                  schedule: int = 0) -> dict:
+                  schedule: int = 0, pending_lens=None) -> dict:
     L = wl.layers[layer]
     return dict(
         mixed_qkv=L.mixed_qkv, raw_gate=L.raw_gate, raw_beta=L.raw_beta,
@@ -30,16 +30,17 @@ def verify_kwargs(wl: Workload, layer: int, counter: torch.Tensor,
         spec_query_len=wl.Q, conv_dim_first=wl.conv_dim_first,
         work_counter=counter, record_rows=wl.record_rows,
         null_block_id=wl.null_block_id, max_workgroups=max_workgroups,
-        items_per_ticket=items_per_ticket, schedule=schedule)
+        items_per_ticket=items_per_ticket, schedule=schedule,
+        pending_lens=pending_lens)
 
 
 def verify(wl: Workload, layer: int, counter: torch.Tensor,
            max_workgroups: int = 0, items_per_ticket: int = 0,
-           stream=None, schedule: int = 0) -> None:
+           stream=None, schedule: int = 0, pending_lens=None) -> None:
     kda.conv_update_verify(stream=stream,
                            **verify_kwargs(wl, layer, counter,
                                            max_workgroups, items_per_ticket,
-                                           schedule))
+                                           schedule, pending_lens))
 
 
 def commit_context(wl: Workload, layers: Optional[list] = None
