@@ -231,6 +231,15 @@ int kda_check_verify(const kda_verify_args* args);
    unchanged; null requests get +0.0 outputs and nothing else. */
 int kda_conv_update_verify(const kda_verify_args* args, void* stream);
 
+/* The unfused verify (ops page, `kda_recoverssm_verify` and
+   `_kda_recoverssm_verify_kernel`): the same as kda_conv_update_verify
+   except that mixed_qkv [T, 3HD] already holds the convolved q | k | v
+   (the three column blocks, channel = part*H*D + h*D + d) and the key
+   record stores that k as given.  conv_state, conv_weight and
+   num_accepted_tokens are not used (they may be empty / NULL). */
+int kda_check_verify_qkv(const kda_verify_args* args);
+int kda_recoverssm_verify_qkv(const kda_verify_args* args, void* stream);
+
 /* Host-only validation of commit arguments (ops page
    `KDARecoverSSMCommitContext.create` and `.commit`). */
 int kda_check_commit(const kda_commit_args* args);

@@ -10,8 +10,10 @@ from .ops import (  # noqa: F401
     KdaUnaligned,
     abi_version,
     check_verify,
+    check_verify_qkv,
     conv_update_verify,
     describe,
     reset_counter,
     verify_args,
+    verify_qkv,
 )

@@ -29,7 +29,8 @@ KDA_BF16 = 1
 
 EXPORTED = (
     "kda_abi_version", "kda_last_error", "kda_status_string",
-    "kda_check_verify", "kda_conv_update_verify", "kda_check_commit",
+    "kda_check_verify", "kda_conv_update_verify", "kda_check_verify_qkv",
+    "kda_recoverssm_verify_qkv", "kda_check_commit",
     "kda_recoverssm_commit", "kda_reset_counter",
 )
 
@@ -106,6 +107,11 @@ def load() -> ctypes.CDLL:
     lib.kda_check_verify.argtypes = [POINTER(KdaVerifyArgs)]
     lib.kda_conv_update_verify.restype = c_int
     lib.kda_conv_update_verify.argtypes = [POINTER(KdaVerifyArgs), c_void_p]
+    lib.kda_check_verify_qkv.restype = c_int
+    lib.kda_check_verify_qkv.argtypes = [POINTER(KdaVerifyArgs)]
+    lib.kda_recoverssm_verify_qkv.restype = c_int
+    lib.kda_recoverssm_verify_qkv.argtypes = [POINTER(KdaVerifyArgs),
+                                              c_void_p]
     lib.kda_check_commit.restype = c_int
     lib.kda_check_commit.argtypes = [POINTER(KdaCommitArgs)]
     lib.kda_recoverssm_commit.restype = c_int

@@ -83,7 +83,10 @@ struct VerifyPlan {
     if (rc_ != KDA_OK) return rc_; \
   } while (0)
 
-int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
+// conv: the fused conv update (kda_conv_update_verify); otherwise mixed_qkv
+// already holds the convolved q | k | v (kda_recoverssm_verify_qkv) and the
+// conv state, taps and accepted counts are not used.
+int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
   if (a == nullptr) return fail(KDA_E_ARG, "verify arguments are NULL");
   if (a->batch < 0) return fail(KDA_E_ARG, "batch is negative");
   const int64_t Q = a->spec_query_len;
@@ -189,32 +192,36 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
     return fail(KDA_E_LAYOUT, "record rows must be contiguous");
 
   // Conv state and weight.
-  KDA_TRY(check_desc(a->conv_state, "conv_state", 3));
-  KDA_TRY(check_desc(a->conv_weight, "conv_weight", 2));
-  const kda_tensor& cs = a->conv_state;
+  const kda_tensor no_tensor{};
+  const kda_tensor& cs = conv ? a->conv_state : no_tensor;
+  const kda_tensor& cw = conv ? a->conv_weight : no_tensor;
   const int64_t C3 = 3 * HD;
-  const int64_t Lc = a->conv_dim_first ? cs.shape[2] : cs.shape[1];
-  const int64_t cdim = a->conv_dim_first ? cs.shape[1] : cs.shape[2];
-  if (cs.shape[0] != N || cdim != C3)
-    return fail(KDA_E_SHAPE,
-                "conv state must be [slots=%lld, %lld, Lc] (dim first) or "
-                "[slots, Lc, %lld] (token first)",
-                (long long)N, (long long)C3, (long long)C3);
-  if (cs.dtype != act)
-    return fail(KDA_E_DTYPE,
-                "the conv state must use the activation dtype (%s)",
-                dt_name(act));
-  if (Lc - Q + 2 != kda::kConvWidth)
-    return fail(KDA_E_UNSUPPORTED,
-                "conv state length %lld implies a width-%lld convolution; "
-                "only width %d is supported (length = Q + 2)",
-                (long long)Lc, (long long)(Lc - Q + 2), kda::kConvWidth);
-  if (!shape_is(a->conv_weight, C3, kda::kConvWidth))
-    return fail(KDA_E_SHAPE, "conv_weight must be [%lld, %d]",
-                (long long)C3, kda::kConvWidth);
-  if (a->conv_weight.dtype != KDA_F32 && a->conv_weight.dtype != act)
-    return fail(KDA_E_DTYPE,
-                "conv_weight must be float32 or the activation dtype");
+  const int64_t Lc = !conv ? 0 : a->conv_dim_first ? cs.shape[2] : cs.shape[1];
+  if (conv) {
+    KDA_TRY(check_desc(a->conv_state, "conv_state", 3));
+    KDA_TRY(check_desc(a->conv_weight, "conv_weight", 2));
+    const int64_t cdim = a->conv_dim_first ? cs.shape[1] : cs.shape[2];
+    if (cs.shape[0] != N || cdim != C3)
+      return fail(KDA_E_SHAPE,
+                  "conv state must be [slots=%lld, %lld, Lc] (dim first) or "
+                  "[slots, Lc, %lld] (token first)",
+                  (long long)N, (long long)C3, (long long)C3);
+    if (cs.dtype != act)
+      return fail(KDA_E_DTYPE,
+                  "the conv state must use the activation dtype (%s)",
+                  dt_name(act));
+    if (Lc - Q + 2 != kda::kConvWidth)
+      return fail(KDA_E_UNSUPPORTED,
+                  "conv state length %lld implies a width-%lld convolution; "
+                  "only width %d is supported (length = Q + 2)",
+                  (long long)Lc, (long long)(Lc - Q + 2), kda::kConvWidth);
+    if (!shape_is(a->conv_weight, C3, kda::kConvWidth))
+      return fail(KDA_E_SHAPE, "conv_weight must be [%lld, %d]",
+                  (long long)C3, kda::kConvWidth);
+    if (a->conv_weight.dtype != KDA_F32 && a->conv_weight.dtype != act)
+      return fail(KDA_E_DTYPE,
+                  "conv_weight must be float32 or the activation dtype");
+  }
 
   // Capacity (ops page: more tokens than the window allows is an error).
   if (T > int64_t(a->batch) * Q)
@@ -227,8 +234,7 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
 
   // Static tensors: 16-byte starts (kernels page `_check_layouts`).
   const kda_tensor* statics[] = {&a->state, &a->A_log, &a->dt_bias,
-                                 &a->correction, &a->key_gate,
-                                 &a->conv_state, &a->conv_weight};
+                                 &a->correction, &a->key_gate, &cs, &cw};
   const char* snames[] = {"state", "A_log", "dt_bias", "correction",
                           "key_gate", "conv_state", "conv_weight"};
   for (int i = 0; i < 7; ++i)
@@ -266,7 +272,8 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
   if (a->schedule < KDA_SCHEDULE_DEFAULT || a->schedule > KDA_SCHEDULE_TICKETS)
     return fail(KDA_E_ARG, "unknown schedule %d", a->schedule);
   if (a->batch > 0) {
-    if (!a->query_start_loc || !a->state_indices || !a->num_accepted_tokens)
+    if (!a->query_start_loc || !a->state_indices ||
+        (conv && !a->num_accepted_tokens))
       return fail(KDA_E_ARG,
                   "query_start_loc, state_indices and num_accepted_tokens "
                   "are required");
@@ -293,14 +300,13 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
       S.stride[0], a->correction.stride[0], a->correction.stride[1],
       a->correction.stride[2], a->key_gate.stride[0], a->key_gate.stride[1],
       a->key_gate.stride[2], a->out.stride[0], cs.stride[0], cs.stride[1],
-      cs.stride[2], a->conv_weight.stride[0], a->conv_weight.stride[1]};
+      cs.stride[2], cw.stride[0], cw.stride[1]};
   for (int64_t st : strides)
     if (st < 0 || st > i32max)
       return fail(KDA_E_LAYOUT, "a tensor stride is negative or exceeds 2^31");
   const int64_t s_chan = a->conv_dim_first ? cs.stride[1] : cs.stride[2];
   const int64_t s_tok = a->conv_dim_first ? cs.stride[2] : cs.stride[1];
-  if (C3 * s_chan + Lc * s_tok > i32max ||
-      C3 * a->conv_weight.stride[0] > i32max ||
+  if (C3 * s_chan + Lc * s_tok > i32max || C3 * cw.stride[0] > i32max ||
       Q * (a->mixed_qkv.stride[0] + a->raw_gate.stride[0] +
            a->raw_beta.stride[0] + a->out.stride[0]) > i32max)
     return fail(KDA_E_LAYOUT, "per-request offsets exceed 2^31 elements");
@@ -331,12 +337,12 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
   p.s_cs_slot = int32_t(cs.stride[0]);
   p.s_cs_chan = int32_t(s_chan);
   p.s_cs_tok = int32_t(s_tok);
-  p.conv_weight = a->conv_weight.data;
-  p.s_w_chan = int32_t(a->conv_weight.stride[0]);
-  p.s_w_tap = int32_t(a->conv_weight.stride[1]);
+  p.conv_weight = cw.data;
+  p.s_w_chan = int32_t(cw.stride[0]);
+  p.s_w_tap = int32_t(cw.stride[1]);
   p.qsl = a->query_start_loc;
   p.slots = a->state_indices;
-  p.accepted = a->num_accepted_tokens;
+  p.accepted = conv ? a->num_accepted_tokens : a->state_indices;
   p.record_rows = a->record_rows;
   p.pending = a->pending_lens;
   p.counter = a->work_counter;
@@ -349,9 +355,11 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan) {
   p.null_id = a->null_block_id;
   p.flags = (a->out.dtype == KDA_BF16 ? kda::kOutBf16 : 0) |
             (a->key_gate.dtype == KDA_BF16 ? kda::kKgBf16 : 0) |
-            (a->conv_weight.dtype == KDA_BF16 ? kda::kWBf16 : 0) |
+            (conv && cw.dtype == KDA_BF16 ? kda::kWBf16 : 0) |
+            (conv ? 0 : kda::kNoConv) |
             (a->use_lower_bound ? kda::kLowerBound : 0);
-  if (a->conv_dim_first && s_tok == 1 && (Q == 4 || Q == 8 || Q == 16) &&
+  if (conv && a->conv_dim_first && s_tok == 1 &&
+      (Q == 4 || Q == 8 || Q == 16) &&
       (Lc * ea) % 4 == 0 && (s_chan * ea) % 4 == 0 &&
       (cs.stride[0] * ea) % 4 == 0)
     p.flags |= kda::kConvRow;
@@ -502,13 +510,30 @@ const char* kda_status_string(int status) {
 int kda_check_verify(const kda_verify_args* args) {
   g_err.clear();
   VerifyPlan plan;
-  return plan_verify(args, &plan);
+  return plan_verify(args, &plan, true);
+}
+
+int kda_check_verify_qkv(const kda_verify_args* args) {
+  g_err.clear();
+  VerifyPlan plan;
+  return plan_verify(args, &plan, false);
+}
+
+int kda_recoverssm_verify_qkv(const kda_verify_args* args, void* stream) {
+  g_err.clear();
+  VerifyPlan plan;
+  KDA_TRY(plan_verify(args, &plan, false));
+  if (plan.noop) return KDA_OK;
+  return device_status(
+      kda::launch_verify(plan.p, plan.D, plan.act_bf16, plan.schedule,
+                         plan.grid, static_cast<hipStream_t>(stream)),
+      "kda_recoverssm_verify_qkv launch");
 }
 
 int kda_conv_update_verify(const kda_verify_args* args, void* stream) {
   g_err.clear();
   VerifyPlan plan;
-  KDA_TRY(plan_verify(args, &plan));
+  KDA_TRY(plan_verify(args, &plan, true));
   if (plan.noop) return KDA_OK;
   return device_status(
       kda::launch_verify(plan.p, plan.D, plan.act_bf16, plan.schedule,

@@ -52,6 +52,8 @@ constexpr int32_t kLowerBound = 8;
 // dim-first conv state whose rows (Q + 2 elements, Q in {4, 8, 16}) are
 // contiguous and 4-byte aligned: read and rolled a whole row at a time
 constexpr int32_t kConvRow = 16;
+// mixed_qkv already holds the convolved q | k | v: no conv, no roll
+constexpr int32_t kNoConv = 64;
 
 struct CommitParams {
   const int64_t* state_base;  const int64_t* state_bs;

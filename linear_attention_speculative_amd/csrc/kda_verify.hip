@@ -195,10 +195,13 @@ __device__ __forceinline__ void load_head(const VerifyParams& p, int h,
   const int tid = fresh_tid();
   const int HD = p.H * D;
   const bool w_bf16 = (p.flags & kWBf16) != 0;
+  const bool conv = (p.flags & kNoConv) == 0;
 #pragma unroll
   for (int jj = 0; jj < C::JC; ++jj) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hr.w[jj][i] = 0;
     const int j = tid + jj * C::NT;
-    if (j < 3 * D) {
+    if (conv && j < 3 * D) {
       const int part = j / D, d = j - part * D;
       const uint32_t wo = (part * HD + h * D + d) * p.s_w_chan;
 #pragma unroll
@@ -275,6 +278,7 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
   const bool kg_bf16 = (p.flags & kKgBf16) != 0;
   const bool w_bf16 = (p.flags & kWBf16) != 0;
   const bool row_fast = (p.flags & kConvRow) != 0;
+  const bool conv = (p.flags & kNoConv) == 0;
 
 #pragma unroll
   for (int jj = 0; jj < C::JC; ++jj) {
@@ -302,7 +306,8 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
           acc = fmaf(w[1], s1, acc);
           acc = fmaf(w[2], s2, acc);
           acc = fmaf(w[3], s3, acc);
-          const float yv = acc * sigmoidf_(acc);
+          // (the unfused entry receives the convolved value itself)
+          const float yv = conv ? acc * sigmoidf_(acc) : s3;
           sm.y[part][t][d] = yv;
           if (part == 1 && rec_ok) {
             if (kg_bf16)
@@ -318,7 +323,9 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
       // Roll: the two newest history entries, then the q new inputs, at
       // the front; positions past 2 + q keep their bytes.
       AT* csc = cs + ch * s_cc;
-      if (row_fast) {
+      if (!conv) {
+        // no conv state
+      } else if (row_fast) {
         // the whole row in one pass; its tail is written back unchanged
         constexpr int RE = QMAX + 2;
         constexpr int EW = 4 / int(sizeof(AT));  // elements per dword
@@ -743,7 +750,11 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
       if (j < 3 * D) {
         const int part = j / D, d = j - part * D;
         const int ch = part * HD + h * D + d;
-        if (p.flags & kConvRow) {
+        if (p.flags & kNoConv) {
+          // q | k | v given after the convolution: no history
+#pragma unroll
+          for (int i = 0; i < 3; ++i) s.hist[jj][i] = AT{};
+        } else if (p.flags & kConvRow) {
           const uint32_t* rp = reinterpret_cast<const uint32_t*>(cs + ch * s_cc);
 #pragma unroll
           for (int i = 0; i < Small<D, QMAX, ACT_BF16>::RD; ++i)

@@ -136,6 +136,31 @@ def conv_update_verify(*, stream=None, **kwargs) -> None:
         _raise(rc)
 
 
+def _qkv_args(kwargs) -> _abi.KdaVerifyArgs:
+    for k in ("conv_state", "conv_weight", "num_accepted_tokens"):
+        kwargs.setdefault(k, None)
+    kwargs.setdefault("conv_dim_first", True)
+    return verify_args(**kwargs)
+
+
+def check_verify_qkv(**kwargs) -> int:
+    """Host-only validation of the unfused verify (no launch)."""
+    a = _qkv_args(kwargs)
+    return _abi.load().kda_check_verify_qkv(ctypes.byref(a))
+
+
+def verify_qkv(*, stream=None, **kwargs) -> None:
+    """The unfused verify (ops page, `kda_recoverssm_verify`): `mixed_qkv`
+    holds the already convolved q | k | v; conv_state, conv_weight and
+    num_accepted_tokens are not used (pass None).  Otherwise as
+    `conv_update_verify`."""
+    a = _qkv_args(kwargs)
+    rc = _abi.load().kda_recoverssm_verify_qkv(ctypes.byref(a),
+                                              _stream(stream))
+    if rc != _abi.KDA_OK:
+        _raise(rc)
+
+
 def reset_counter(counter: torch.Tensor, stream=None) -> None:
     rc = _abi.load().kda_reset_counter(_ptr(counter), counter.numel(),
                                       _stream(stream))

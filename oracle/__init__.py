@@ -30,4 +30,5 @@ from .kda import (  # noqa: F401
     round_to,
     sigmoid,
     silu,
+    verify_qkv,
 )

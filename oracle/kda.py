@@ -150,6 +150,47 @@ def conv_update_verify(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
     work to a sample (for checking large workloads); requests are
     independent, so a sample's results equal the full run's.
     """
+    return _verify(
+        mixed_qkv=mixed_qkv, raw_gate=raw_gate, raw_beta=raw_beta,
+        A_log=A_log, dt_bias=dt_bias, state=state, correction=correction,
+        key_gate=key_gate, out=out, conv_state=conv_state,
+        conv_weight=conv_weight, query_start_loc=query_start_loc,
+        state_indices=state_indices, num_accepted_tokens=num_accepted_tokens,
+        spec_query_len=spec_query_len, null_block_id=null_block_id,
+        use_lower_bound=use_lower_bound, lower_bound=lower_bound,
+        record_rows=record_rows, key_gate_dtype=key_gate_dtype, heads=heads,
+        requests=requests)
+
+
+def verify_qkv(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state,
+               correction, key_gate, out, query_start_loc, state_indices,
+               spec_query_len, null_block_id=0, use_lower_bound=False,
+               lower_bound=0.0, record_rows=None, key_gate_dtype="f32",
+               heads=None, requests=None):
+    """The unfused verify (ops page, `kda_recoverssm_verify` with
+    `_kda_recoverssm_verify_kernel`): `mixed_qkv` [T, 3HK] already holds
+    the convolved q | k | v; there is no conv state.  Same per-head steps
+    and records as `conv_update_verify` (the key record is that k).
+    Returns the same dict without `conv_state`."""
+    r = _verify(
+        mixed_qkv=mixed_qkv, raw_gate=raw_gate, raw_beta=raw_beta,
+        A_log=A_log, dt_bias=dt_bias, state=state, correction=correction,
+        key_gate=key_gate, out=out, conv_state=None, conv_weight=None,
+        query_start_loc=query_start_loc, state_indices=state_indices,
+        num_accepted_tokens=None, spec_query_len=spec_query_len,
+        null_block_id=null_block_id, use_lower_bound=use_lower_bound,
+        lower_bound=lower_bound, record_rows=record_rows,
+        key_gate_dtype=key_gate_dtype, heads=heads, requests=requests)
+    del r["conv_state"]
+    return r
+
+
+def _verify(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state,
+            correction, key_gate, out, conv_state, conv_weight,
+            query_start_loc, state_indices, num_accepted_tokens,
+            spec_query_len, null_block_id, use_lower_bound, lower_bound,
+            record_rows, key_gate_dtype, heads, requests):
+    """Both verifies; `conv_state` None means q | k | v come convolved."""
     Q = int(spec_query_len)
     N, H, V, K = state.shape
     R = correction.shape[0]
@@ -158,7 +199,8 @@ def conv_update_verify(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
     out = np.array(out, dtype=np.float64, copy=True)
     correction = np.array(correction, dtype=np.float64, copy=True)
     key_gate = np.array(key_gate, dtype=np.float64, copy=True)
-    conv_state = np.array(conv_state, copy=True)
+    if conv_state is not None:
+        conv_state = np.array(conv_state, copy=True)
     out_written = np.zeros(out.shape, dtype=bool)
     rec_written = np.zeros(correction.shape[:3], dtype=bool)
     hs = np.arange(H) if heads is None else np.asarray(heads)
@@ -178,9 +220,13 @@ def conv_update_verify(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
             continue
         r = int(record_rows[b]) if record_rows is not None else slot
         rec_ok = 0 <= r < R
-        y, conv_state[slot] = conv_update(conv_state[slot],
-                                          mixed_qkv[bos:bos + q], conv_weight,
-                                          num_accepted_tokens[b])
+        if conv_state is not None:
+            y, conv_state[slot] = conv_update(conv_state[slot],
+                                              mixed_qkv[bos:bos + q],
+                                              conv_weight,
+                                              num_accepted_tokens[b])
+        else:
+            y = np.asarray(mixed_qkv[bos:bos + q], np.float64)
         qm = y[:, :HK].reshape(q, H, K)[:, hs]
         km = y[:, HK:2 * HK].reshape(q, H, K)[:, hs]
         vm = y[:, 2 * HK:].reshape(q, H, V)[:, hs]

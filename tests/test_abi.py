@@ -183,6 +183,45 @@ def test_zero_batch_is_a_valid_no_op():
     kda.conv_update_verify(stream=0, **kw)   # returns without launching
 
 
+def _qkv_kw(**over):
+    wl, kw = _kw(**over)
+    for k in ("conv_state", "conv_weight", "num_accepted_tokens"):
+        kw[k] = None
+    return wl, kw
+
+
+def test_unfused_verify_checks():
+    for act in ("f32", "bf16"):
+        wl, kw = _qkv_kw(act=act, weight=act)
+        assert kda.check_verify_qkv(**kw) == 0, kda.load().kda_last_error()
+    # the conv arguments are ignored, whatever they hold
+    wl, kw = _kw()
+    kw["conv_state"] = kw["conv_state"][:, :, :-1]
+    assert kda.check_verify_qkv(**kw) == 0
+    assert _code(kw) == _abi.KDA_E_UNSUPPORTED
+    # the other rules still apply
+    wl, kw = _qkv_kw()
+    kw["query_start_loc"] = None
+    assert kda.check_verify_qkv(**kw) == _abi.KDA_E_ARG
+    wl, kw = _qkv_kw()
+    kw["mixed_qkv"] = kw["mixed_qkv"][:, :-8]
+    assert kda.check_verify_qkv(**kw) == _abi.KDA_E_SHAPE
+    wl, kw = _qkv_kw()
+    kw["state"] = torch.zeros(kw["state"].shape, dtype=torch.bfloat16)
+    assert kda.check_verify_qkv(**kw) == _abi.KDA_E_DTYPE
+    wl, kw = _qkv_kw()
+    kw["schedule"] = _abi.KDA_SCHEDULE_TICKETS
+    kw["work_counter"] = None
+    assert kda.check_verify_qkv(**kw) == _abi.KDA_E_ARG
+    wl, kw = _qkv_kw()
+    x = kw["out"]
+    wide = torch.zeros(x.shape[0], x.shape[1] + 1, dtype=x.dtype)
+    kw["out"] = wide[:, :x.shape[1]]
+    assert kda.check_verify_qkv(**kw) == _abi.KDA_E_UNALIGNED
+    with pytest.raises(kda.KdaUnaligned):
+        kda.verify_qkv(stream=0, **kw)
+
+
 def _commit_ctx(**over):
     wl = make_workload(over.pop("cfg", "large"), B=4, H=2, D=16, Q=8, N=8,
                        gates=[None, -5.0, None], **over)

@@ -12,7 +12,8 @@ import linear_attention_speculative_amd as kda
 import oracle
 from tests.gpu_check import (TOL, bits, check_commit, check_verify,
                              commit_layer_inputs, f64, rel_err,
-                             run_oracle_verify, snapshot)
+                             run_oracle_verify, run_oracle_verify_qkv,
+                             snapshot)
 from workloads import drive, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -471,3 +472,56 @@ def test_commit_schedules_agree_bitwise():
     for other in results[1:]:
         for a, b in zip(results[0], other):
             assert torch.equal(a, b)
+
+
+# ---- the unfused verify (q | k | v already convolved) ------------------------
+
+def _qkv_case(wl, layer=0, reqs=None, sched=0):
+    """The layer's activation rows are taken as convolved q | k | v: outputs
+    and records match the oracle's unfused verify; the checkpoint and the
+    conv state are not touched."""
+    L = wl.layers[layer]
+    sample = snapshot(wl, layer, reqs)
+    state_before = L.state.clone()
+    conv_before = L.conv_state.clone()
+    page_before = L.page.clone()
+    rec_before = None if L.record_page is None else L.record_page.clone()
+    counter = _counter()
+    drive.verify_qkv(wl, layer, counter, schedule=sched)
+    torch.cuda.synchronize()
+    assert int(counter.item()) == 0
+    assert torch.equal(L.state, state_before), "verify wrote the checkpoint"
+    assert torch.equal(L.conv_state, conv_before), "conv state was written"
+    ref = run_oracle_verify_qkv(sample)
+    errs = check_verify(wl, layer, sample, ref)
+    _check_pages(wl, layer, page_before, rec_before)
+    return sample, ref, errs
+
+
+@pytest.mark.parametrize("D,Q,act,gate,sched",
+                         [(128, 4, "bf16", None, 0), (64, 8, "f32", -5.0, 2),
+                          (32, 3, "bf16", None, 1), (16, 16, "f32", -5.0, 0),
+                          (128, 8, "f32", None, 2)])
+def test_unfused_verify(D, Q, act, gate, sched):
+    wl = make_workload("ragged", DEV, B=20, H=3, D=D, Q=Q, N=32, act=act,
+                       weight=act, null_frac=0.15, gates=[gate])
+    sample, ref, errs = _qkv_case(wl, sched=sched)
+    # the records feed the commit exactly as the fused verify's do
+    cerr = _commit_case(wl, {0: (sample, ref)})
+    print("qkv", D, Q, act, gate, sched, errs, cerr)
+
+
+def test_unfused_verify_tiny_and_record_rows():
+    wl = make_workload("tiny", DEV)
+    print("qkv tiny", _qkv_case(wl)[2])
+    wl = make_workload("deferred", DEV, B=40, N=96, out_dtype="act",
+                       kg_dtype="act")
+    for layer in range(2):
+        print("qkv rows", layer, _qkv_case(wl, layer)[2])
+
+
+def test_unfused_verify_headline_sampled():
+    wl = make_workload("headline", DEV)
+    reqs = list(range(0, wl.B, 17)) + [wl.B - 1]
+    sample, ref, errs = _qkv_case(wl, reqs=reqs)
+    print("qkv headline", errs)

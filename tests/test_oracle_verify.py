@@ -141,6 +141,84 @@ def test_tiny_verify_and_commit_match_brute_force(gate, dim_first):
             assert written[slot, h]
 
 
+# ---- the unfused verify -------------------------------------------------------
+
+def _library_qkv(inp, wl):
+    """Each request's q | k | v from the library convolution (torch conv1d +
+    SiLU) over its accepted history and drafts; zero rows for nulls."""
+    y = np.zeros_like(inp["mixed_qkv"])
+    qsl, W = inp["query_start_loc"], wl.W
+    for b in range(wl.B):
+        slot = int(inp["state_indices"][b])
+        bos, eos = int(qsl[b]), int(qsl[b + 1])
+        if eos == bos or slot <= 0 or slot >= wl.N:
+            continue
+        a = int(inp["num_accepted_tokens"][b])
+        cs = inp["conv_state"][slot]
+        stream = np.concatenate([cs[:, a - 1:a + W - 2],
+                                 inp["mixed_qkv"][bos:eos].T], axis=1)
+        y[bos:eos] = oracle.silu(_library_conv(stream, inp["conv_weight"]))
+    return y
+
+
+@pytest.mark.parametrize("cfg,gate", [("ragged", None), ("ragged", -5.0),
+                                      ("deferred", None)])
+def test_unfused_verify_on_convolved_input_equals_fused(cfg, gate):
+    # The unfused verify takes q | k | v already convolved.  Fed the library
+    # convolution of each request's stream, it must reproduce the fused
+    # verify (itself pinned to brute force above) output for output, write
+    # the same masks, and record that k as the key.
+    wl = make_workload(cfg, B=8, H=2, D=8, Q=4, N=12, act="f32",
+                       weight="f32", gates=[gate], null_frac=0.25)
+    inp = _oracle_inputs(wl)
+    fused = oracle.conv_update_verify(**inp)
+    y = _library_qkv(inp, wl)
+    kw = {k: v for k, v in inp.items()
+          if k not in ("conv_state", "conv_weight", "num_accepted_tokens")}
+    kw["mixed_qkv"] = y
+    res = oracle.verify_qkv(**kw)
+    assert "conv_state" not in res
+    for k in ("out_written", "rec_written"):
+        assert np.array_equal(res[k], fused[k]), k
+    np.testing.assert_allclose(res["out"], fused["out"], rtol=1e-10,
+                               atol=1e-12)
+    np.testing.assert_allclose(res["correction"], fused["correction"],
+                               rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(res["key_gate"], fused["key_gate"],
+                               rtol=1e-6, atol=1e-7)
+    # the key record is the given k, rounded to the record dtype only
+    K, H = wl.D, wl.H
+    qsl = inp["query_start_loc"]
+    rows = inp["record_rows"]
+    for b in range(wl.B):
+        slot = int(inp["state_indices"][b])
+        if slot <= 0:
+            continue
+        r = slot if rows is None else int(rows[b])
+        bos, eos = int(qsl[b]), int(qsl[b + 1])
+        for t in range(eos - bos):
+            k = y[bos + t, H * K:2 * H * K].reshape(H, K)
+            assert np.array_equal(res["key_gate"][r, :, t, :K],
+                                  oracle.round_to(k, "f32"))
+
+
+def test_unfused_verify_with_identity_taps_is_silu_of_input():
+    # A conv whose only tap is the newest input (weight [0, 0, 0, 1]) turns
+    # the fused verify into the unfused one applied to SiLU(x).
+    wl = make_workload("ragged", B=6, H=2, D=8, Q=4, N=10, act="f32",
+                       weight="f32", null_frac=0.0)
+    inp = _oracle_inputs(wl)
+    inp["conv_weight"] = np.zeros_like(inp["conv_weight"])
+    inp["conv_weight"][:, -1] = 1.0
+    fused = oracle.conv_update_verify(**inp)
+    kw = {k: v for k, v in inp.items()
+          if k not in ("conv_state", "conv_weight", "num_accepted_tokens")}
+    kw["mixed_qkv"] = oracle.silu(inp["mixed_qkv"])
+    res = oracle.verify_qkv(**kw)
+    for k in ("out", "correction", "key_gate", "out_written", "rec_written"):
+        assert np.array_equal(res[k], fused[k]), k
+
+
 # ---- commit fold identities --------------------------------------------------
 
 @pytest.mark.parametrize("gate", [None, -5.0])

@@ -43,6 +43,29 @@ def verify(wl: Workload, layer: int, counter: torch.Tensor,
                                            schedule, pending_lens))
 
 
+def verify_qkv_kwargs(wl: Workload, layer: int, mixed_qkv: torch.Tensor,
+                      counter=None, **kw) -> dict:
+    """Arguments of the unfused verify: `mixed_qkv` holds the convolved
+    q | k | v of every token; the conv state, taps and accepted counts are
+    left out."""
+    d = verify_kwargs(wl, layer, counter, **kw)
+    for k in ("conv_state", "conv_weight", "num_accepted_tokens",
+              "conv_dim_first"):
+        del d[k]
+    d["mixed_qkv"] = mixed_qkv
+    return d
+
+
+def verify_qkv(wl: Workload, layer: int, counter=None, mixed_qkv=None,
+               stream=None, **kw) -> None:
+    """The unfused verify of `layer`; `mixed_qkv` (default: the layer's
+    activation tensor) is taken as the convolved q | k | v."""
+    L = wl.layers[layer]
+    kda.verify_qkv(stream=stream, **verify_qkv_kwargs(
+        wl, layer, L.mixed_qkv if mixed_qkv is None else mixed_qkv,
+        counter, **kw))
+
+
 def commit_context(wl: Workload, layers: Optional[list] = None
                    ) -> kda.CommitContext:
     idx = range(len(wl.layers)) if layers is None else layers
