@@ -15,12 +15,16 @@ Parity status: every function below is pinned by the `-m "not gpu"` tests in
 tests/test_oracle_*.py (closed forms, special cases, a library convolution,
 a brute-force scalar implementation, an exact rational-arithmetic case and
 the algebraic identity between the verify recurrence and the commit fold).
+The commit plan, the boundary fold and the conv compaction are pinned by
+multi-step simulations against a fresh recurrence over the accepted stream.
 """
 from .kda import (  # noqa: F401
     EPS,
     SOFTPLUS_THRESHOLD,
     commit,
     commit_fold_reverse,
+    commit_plan,
+    compact_conv_state,
     conv_update,
     conv_update_verify,
     delta_step,

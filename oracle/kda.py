@@ -256,6 +256,7 @@ def _verify(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state,
 
 def commit(*, layers, state_indices, commit_lens, spec_query_len,
            null_block_id=0, final_state_indices=None, record_rows=None,
+           boundary_state_indices=None, boundary_recovery_lens=None,
            heads=None, requests=None):
     """Fold each request's first n accepted positions into its checkpoint,
     for every layer (ops page, `_commit_kda_state_kernel` and
@@ -272,6 +273,13 @@ def commit(*, layers, state_indices, commit_lens, spec_query_len,
     [R,H,Q,V], `key_gate` [R,H,Q,2K], `A_log` [H], `dt_bias` [H,K] and
     `use_lower_bound`, `lower_bound`.  Returns a list of (new state, written
     mask [N, H]).  `heads` / `requests` restrict the work to a sample.
+
+    Align mode (ops page, `_commit_kda_state_kernel` with ALIGN_MODE):
+    when `boundary_state_indices` is given, a request that commits also
+    stores the state after its first m = boundary_recovery_lens[b] (clamped
+    to [0, n]) positions at its boundary slot, if that slot is live.  Every
+    state is computed from the source checkpoint as it was before the
+    launch; the boundary is stored before the final state.
     """
     Q = int(spec_query_len)
     results = []
@@ -299,7 +307,12 @@ def commit(*, layers, state_indices, commit_lens, spec_query_len,
             r = int(record_rows[b]) if record_rows is not None else slot
             if not 0 <= r < R:
                 continue
+            bslot, m = null_block_id, 0
+            if boundary_state_indices is not None:
+                bslot = int(boundary_state_indices[b])
+                m = min(max(int(boundary_recovery_lens[b]), 0), n)
             S = np.asarray(state[slot][hs], dtype=np.float64)
+            at_boundary = S
             for t in range(n):
                 kg = layer["key_gate"][r, hs, t]
                 khat = l2_normalize(kg[:, :K])
@@ -307,6 +320,11 @@ def commit(*, layers, state_indices, commit_lens, spec_query_len,
                              layer["use_lower_bound"], layer["lower_bound"])
                 c = layer["correction"][r, hs, t]
                 S = S * np.exp(g)[:, None, :] + c[:, :, None] * khat[:, None, :]
+                if t + 1 == m:
+                    at_boundary = S
+            if null_block_id < bslot < N:
+                new[bslot, hs] = round_to(at_boundary, "f32")
+                written[bslot, hs] = True
             new[f, hs] = round_to(S, "f32")
             written[f, hs] = True
         results.append((new, written))
@@ -334,3 +352,106 @@ def commit_fold_reverse(S0, corrections, keys, raw_gates, dt_bias, A,
         acc += np.outer(corrections[t], khat) * later_decay[None, :]
         later_decay = later_decay * d
     return S0 * later_decay[None, :] + acc
+
+
+def commit_plan(*, num_accepted_tokens, state_indices, query_start_loc,
+                spec_query_len, null_block_id=0, request_indices=None,
+                block_table=None, num_computed_tokens=None,
+                mamba_block_size=None):
+    """Per-request commit plan (ops page, `_prepare_commit_plan_kernel` as
+    launched by `KDARecoverSSMCommitContext.commit`; its body is not on the
+    pages, so this is the reading stated here).
+
+    Row b of the batch reads its per-request values (accepted count, block
+    table row, computed-token count) at row request_indices[b] (default b);
+    its state slot and window at b.  Then
+      n = accepted count clamped to [0, q_b]   (0 for a null slot);
+    without a block table: final = source slot, no boundary;
+    with one (prefix caching, one state block per `mamba_block_size` = bs
+    tokens), for c = computed tokens before the window and end = c + n:
+      final = block_table[row, end // bs], the block of the next token to
+              compute, which holds the running checkpoint (null if past the
+              table);
+      if that block starts at P with c < P <= end, the committed tokens
+      completed the block before it: boundary = block_table[row, P/bs - 1]
+      receives the state after its last token, i.e. after P - c positions
+      (all n of them when P = end: then both blocks get the same state).
+    Since bs >= Q, one window completes at most one block.  The running
+    block is always the incomplete one, so the verify's in-place conv roll
+    (at the source, the block of token c) never touches a completed block.
+    Returns int arrays (commit_lens, final, boundary, boundary_lens).
+    """
+    Q = int(spec_query_len)
+    B = len(state_indices)
+    qsl = np.asarray(query_start_loc)
+    lens = np.zeros(B, dtype=np.int64)
+    final = np.array(state_indices, dtype=np.int64, copy=True)
+    boundary = np.full(B, null_block_id, dtype=np.int64)
+    blens = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        row = b if request_indices is None else int(request_indices[b])
+        q = min(max(int(qsl[b + 1]) - int(qsl[b]), 0), Q)
+        n = min(max(int(num_accepted_tokens[row]), 0), q)
+        if int(state_indices[b]) <= null_block_id:
+            n = 0
+        lens[b] = n
+        if block_table is None or n == 0:
+            continue
+        bs = int(mamba_block_size)
+        c = max(int(num_computed_tokens[row]), 0)
+        last = (c + n) // bs
+        width = np.asarray(block_table).shape[1]
+        final[b] = int(block_table[row][last]) if last < width \
+            else null_block_id
+        start = last * bs
+        if c < start:
+            boundary[b] = int(block_table[row][last - 1])
+            blens[b] = start - c
+    return lens, final, boundary, blens
+
+
+def compact_conv_state(*, conv_states, state_indices, commit_lens,
+                       final_state_indices, null_block_id=0,
+                       boundary_state_indices=None,
+                       boundary_recovery_lens=None):
+    """Conv-state compaction at commit (ops page, `_compact_conv_state_kernel`
+    as launched by `KDARecoverSSMCommitContext.commit`; body not on the
+    pages, reading stated here).
+
+    With the verify's rolled layout (entry 2 + t holds the window's input t,
+    entries 0 and 1 the two inputs before it), the history after the first
+    n committed positions is entries [n - 1, n - 1 + W - 1).  It is copied
+    to entries [0, W - 1) of the final slot, so that the next verify reads
+    it with accepted count 1; in align mode, the history after m boundary
+    positions (m >= 1) goes to the boundary slot the same way.  Other
+    entries are left as they are; everything is read before anything is
+    written; the boundary is written before the final slot.
+
+    conv_states: per layer, the dim-first logical view [N, C, Lc] (any
+    dtype: values are moved, not computed).  Returns updated copies.
+    """
+    out = []
+    for cs in conv_states:
+        cs = np.asarray(cs)
+        N, _, Lc = cs.shape
+        new = cs.copy()
+        for b in range(len(state_indices)):
+            slot = int(state_indices[b])
+            if slot <= null_block_id or slot >= N:
+                continue
+            Qm = Lc - 2
+            n = min(max(int(commit_lens[b]), 0), Qm)
+            if n == 0:
+                continue
+            f = int(final_state_indices[b])
+            if f <= null_block_id or f >= N:
+                continue
+            hist_n = cs[slot][:, n - 1:n + 2].copy()
+            if boundary_state_indices is not None:
+                bslot = int(boundary_state_indices[b])
+                m = min(max(int(boundary_recovery_lens[b]), 0), n)
+                if null_block_id < bslot < N and m >= 1:
+                    new[bslot][:, 0:3] = cs[slot][:, m - 1:m + 2]
+            new[f][:, 0:3] = hist_n
+        out.append(new)
+    return out
