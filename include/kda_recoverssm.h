@@ -19,9 +19,15 @@
  *
  *   kda_recoverssm_commit   -- folds each request's first n accepted
  *       positions, from those records, into its checkpoint state, for every
- *       layer in one launch.
+ *       layer in one launch; in align mode (prefix caching) it also stores
+ *       the state at a completed block boundary.
  *       (kernels page, function `cute_recoverssm_commit`; ops page,
  *       `_commit_kda_state_kernel` and `KDARecoverSSMCommitContext`.)
+ *
+ *   kda_commit_plan, kda_compact_conv_state -- the two launches that the
+ *       ops page's `KDARecoverSSMCommitContext.commit` runs before the
+ *       state commit: the per-request plan (commit lengths, final and
+ *       boundary slots) and the conv-state compaction.
  *
  * plus host-only argument checks mirroring the pages' validation
  * (kernels page `_check_layouts`, `can_use_cute_recoverssm`; ops page
@@ -35,7 +41,7 @@
  *  - The caller owns every buffer.  The library allocates no device memory,
  *    keeps no pointer after a call returns and performs no host/device
  *    synchronisation.  Launches are asynchronous on the given stream (a
- *    hipStream_t passed as void*; NULL = the null stream), so both launches
+ *    hipStream_t passed as void*; NULL = the null stream), so every launch
  *    may be captured in a HIP graph.
  *  - Every entry point returns KDA_OK (0) or a kda_status code; a failing
  *    call launches nothing and leaves a message for kda_last_error() in the
@@ -60,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 /* Status codes. */
 typedef enum {
@@ -208,7 +214,87 @@ typedef struct {
      correction strides, key/gate bases, key/gate strides).  When given,
      the checks verify every layer's alignment; NULL skips those checks. */
   const int64_t* host_tables;
+  /* Align mode (ops page `_commit_kda_state_kernel` with ALIGN_MODE): both
+     NULL, or both device int32 [batch].  A request that commits and whose
+     boundary slot is live also stores, before its final state, the state
+     after its first m = boundary_recovery_lens[b] (clamped to [0, n])
+     positions at that slot.  Both states come from the source checkpoint
+     as it was before the launch; a request's boundary and final slots must
+     not be another request's source or destination in the same launch. */
+  const int32_t* boundary_state_indices;
+  const int32_t* boundary_recovery_lens;
 } kda_commit_args;
+
+/* Arguments of kda_commit_plan (ops page: `_prepare_commit_plan_kernel`,
+   launched by `KDARecoverSSMCommitContext.commit`; its body is not on the
+   pages).  For row b of the batch, with row = request_indices[b] (or b):
+     n = num_accepted_tokens[row] clamped to [0, q_b], q_b the window of b
+         (0 when state_indices[b] <= null_block_id);
+   without a block table: final = state_indices[b], boundary = null id,
+   boundary length 0.  With one (prefix caching, one state block per
+   mamba_block_size tokens), for c = num_computed_tokens[row] (tokens before
+   the window, clamped to >= 0) and n >= 1:
+     final = block_table[row][(c + n) / bs], the block that will hold the
+             next token (null id when past the table's width);
+     when that block starts at P with c < P (the committed tokens completed
+     the block before it) and P / bs - 1 is inside the table,
+     boundary = block_table[row][P / bs - 1] with boundary length P - c;
+     otherwise boundary = null id, length 0.
+   A row outside [0, num_request_rows) plans no commit (n = 0). */
+typedef struct {
+  int32_t batch;
+  int32_t spec_query_len;          /* Q */
+  int32_t null_block_id;
+  int32_t mamba_block_size;        /* align mode: tokens per block, >= Q */
+  int32_t num_request_rows;        /* rows of the per-request arrays */
+  int32_t block_table_width;       /* align mode: blocks per row */
+  int64_t block_table_strides[2];  /* align mode: row, column (elements) */
+  const int32_t* num_accepted_tokens;  /* device, per request row */
+  const int32_t* request_indices;      /* device [batch] or NULL */
+  const int32_t* state_indices;        /* device [batch] */
+  const int32_t* query_start_loc;      /* device [batch + 1] */
+  const int32_t* block_table;          /* device or NULL (no align) */
+  const int32_t* num_computed_tokens;  /* device per request row, or NULL;
+                                          given iff block_table is */
+  int32_t* commit_lens;                /* device [batch] outputs */
+  int32_t* final_state_indices;
+  int32_t* boundary_state_indices;
+  int32_t* boundary_recovery_lens;
+} kda_plan_args;
+
+/* Arguments of kda_compact_conv_state (ops page: `_compact_conv_state_kernel`,
+   launched by `KDARecoverSSMCommitContext.commit`; its body is not on the
+   pages).  The verify leaves a request's conv state rolled: entry 2 + t
+   holds window input t, entries 0 and 1 the two inputs before the window.
+   For every layer and every request with a live source slot, n =
+   commit_lens[b] (clamped to [0, Q]) >= 1 and a live final slot, entries
+   [n - 1, n + 2) of the source (the three inputs before token n of the
+   window) are copied to entries [0, 3) of the final slot, so that the next
+   verify reads its history with accepted count 1.  In align mode the
+   entries [m - 1, m + 2) go to a live boundary slot the same way, when
+   m = boundary_recovery_lens[b] (clamped to [0, n]) >= 1.  Other entries
+   are not touched; values are copied bit for bit; everything is read
+   before anything is written, and the boundary is written first. */
+typedef struct {
+  int32_t num_layers;
+  int32_t batch;
+  int32_t spec_query_len;       /* Q: the conv state holds Q + 2 entries */
+  int32_t null_block_id;
+  int64_t num_slots;            /* N */
+  int64_t conv_dim;             /* channels, 3 * H * D */
+  int32_t conv_dtype;           /* kda_dtype of every layer's conv state */
+  int32_t pad_;
+  /* device int64 [4][L]: per layer, the base byte address, then the slot,
+     channel and token strides (elements) of its conv state seen dim-first
+     as [N, conv_dim, Q + 2] (a token-first state is its transpose). */
+  const int64_t* conv_tables;
+  const int64_t* host_conv_tables;  /* optional HOST copy, for the checks */
+  const int32_t* state_indices;           /* device [batch] */
+  const int32_t* commit_lens;             /* device [batch] */
+  const int32_t* final_state_indices;     /* device [batch] or NULL */
+  const int32_t* boundary_state_indices;  /* both NULL or both given */
+  const int32_t* boundary_recovery_lens;
+} kda_compact_args;
 
 /* Library ABI version (KDA_ABI_VERSION). */
 int kda_abi_version(void);
@@ -250,6 +336,16 @@ int kda_check_commit(const kda_commit_args* args);
    becomes S_n = S_0 * prod_t diag(exp g_t) + sum_t c_t k_hat_t^T
    * prod_{s>t} diag(exp g_s) over t < n, stored at the final slot. */
 int kda_recoverssm_commit(const kda_commit_args* args, void* stream);
+
+/* Host-only validation of the plan arguments, then its launch on `stream`
+   (one thread per request; writes only the four output arrays). */
+int kda_check_commit_plan(const kda_plan_args* args);
+int kda_commit_plan(const kda_plan_args* args, void* stream);
+
+/* Host-only validation of the compaction arguments, then its launch on
+   `stream` (one thread per layer, request and channel). */
+int kda_check_compact_conv(const kda_compact_args* args);
+int kda_compact_conv_state(const kda_compact_args* args, void* stream);
 
 /* Launch a one-workgroup kernel that sets counter[0..n) to 0 on `stream`
    (for a counter left non-zero by an aborted launch).  Uses no memset

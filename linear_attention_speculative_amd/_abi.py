@@ -31,7 +31,8 @@ EXPORTED = (
     "kda_abi_version", "kda_last_error", "kda_status_string",
     "kda_check_verify", "kda_conv_update_verify", "kda_check_verify_qkv",
     "kda_recoverssm_verify_qkv", "kda_check_commit",
-    "kda_recoverssm_commit", "kda_reset_counter",
+    "kda_recoverssm_commit", "kda_check_commit_plan", "kda_commit_plan",
+    "kda_check_compact_conv", "kda_compact_conv_state", "kda_reset_counter",
 )
 
 
@@ -80,6 +81,37 @@ class KdaCommitArgs(Structure):
         ("state_indices", c_void_p), ("commit_lens", c_void_p),
         ("final_state_indices", c_void_p), ("record_rows", c_void_p),
         ("host_tables", POINTER(c_int64)),
+        ("boundary_state_indices", c_void_p),
+        ("boundary_recovery_lens", c_void_p),
+    ]
+
+
+class KdaPlanArgs(Structure):
+    _fields_ = [
+        ("batch", c_int32), ("spec_query_len", c_int32),
+        ("null_block_id", c_int32), ("mamba_block_size", c_int32),
+        ("num_request_rows", c_int32), ("block_table_width", c_int32),
+        ("block_table_strides", c_int64 * 2),
+        ("num_accepted_tokens", c_void_p), ("request_indices", c_void_p),
+        ("state_indices", c_void_p), ("query_start_loc", c_void_p),
+        ("block_table", c_void_p), ("num_computed_tokens", c_void_p),
+        ("commit_lens", c_void_p), ("final_state_indices", c_void_p),
+        ("boundary_state_indices", c_void_p),
+        ("boundary_recovery_lens", c_void_p),
+    ]
+
+
+class KdaCompactArgs(Structure):
+    _fields_ = [
+        ("num_layers", c_int32), ("batch", c_int32),
+        ("spec_query_len", c_int32), ("null_block_id", c_int32),
+        ("num_slots", c_int64), ("conv_dim", c_int64),
+        ("conv_dtype", c_int32), ("pad_", c_int32),
+        ("conv_tables", c_void_p), ("host_conv_tables", POINTER(c_int64)),
+        ("state_indices", c_void_p), ("commit_lens", c_void_p),
+        ("final_state_indices", c_void_p),
+        ("boundary_state_indices", c_void_p),
+        ("boundary_recovery_lens", c_void_p),
     ]
 
 
@@ -116,6 +148,14 @@ def load() -> ctypes.CDLL:
     lib.kda_check_commit.argtypes = [POINTER(KdaCommitArgs)]
     lib.kda_recoverssm_commit.restype = c_int
     lib.kda_recoverssm_commit.argtypes = [POINTER(KdaCommitArgs), c_void_p]
+    lib.kda_check_commit_plan.restype = c_int
+    lib.kda_check_commit_plan.argtypes = [POINTER(KdaPlanArgs)]
+    lib.kda_commit_plan.restype = c_int
+    lib.kda_commit_plan.argtypes = [POINTER(KdaPlanArgs), c_void_p]
+    lib.kda_check_compact_conv.restype = c_int
+    lib.kda_check_compact_conv.argtypes = [POINTER(KdaCompactArgs)]
+    lib.kda_compact_conv_state.restype = c_int
+    lib.kda_compact_conv_state.argtypes = [POINTER(KdaCompactArgs), c_void_p]
     lib.kda_reset_counter.restype = c_int
     lib.kda_reset_counter.argtypes = [c_void_p, c_int32, c_void_p]
     _LIB = lib

@@ -406,6 +406,10 @@ int plan_commit(const kda_commit_args* a, CommitPlan* plan) {
     return fail(KDA_E_ARG, "the stacked gate parameters are required");
   if (a->batch > 0 && (!a->state_indices || !a->commit_lens))
     return fail(KDA_E_ARG, "state_indices and commit_lens are required");
+  if (!a->boundary_state_indices != !a->boundary_recovery_lens)
+    return fail(KDA_E_ARG,
+                "KDA RecoverSSM align metadata is incomplete: boundary slots "
+                "and boundary lengths go together");
   if (a->state_strides[0] != D * D || a->state_strides[1] != D)
     return fail(KDA_E_LAYOUT,
                 "KDA RecoverSSM layers need contiguous checkpoint heads "
@@ -464,6 +468,8 @@ int plan_commit(const kda_commit_args* a, CommitPlan* plan) {
   p.commit_lens = a->commit_lens;
   p.final_slots = a->final_state_indices;
   p.record_rows = a->record_rows;
+  p.bnd_slots = a->boundary_state_indices;
+  p.bnd_lens = a->boundary_recovery_lens;
   p.L = a->num_layers;
   p.B = a->batch;
   p.H = int32_t(H);
@@ -475,6 +481,136 @@ int plan_commit(const kda_commit_args* a, CommitPlan* plan) {
   p.grid = a->max_workgroups;
   plan->D = int(D);
   plan->noop = a->batch == 0;
+  return KDA_OK;
+}
+
+// Commit plan (ops page `KDARecoverSSMCommitContext.commit` checks: align
+// arguments all or none, a block that covers one window, a 2-D table).
+int plan_plan(const kda_plan_args* a, kda::PlanParams* p) {
+  if (a == nullptr) return fail(KDA_E_ARG, "plan arguments are NULL");
+  if (a->batch < 0) return fail(KDA_E_ARG, "batch is negative");
+  if (a->spec_query_len < 1 || a->spec_query_len > kda::kMaxWindow)
+    return fail(KDA_E_UNSUPPORTED,
+                "KDA RecoverSSM supports windows of 1 to %d",
+                kda::kMaxWindow);
+  const bool align = a->block_table != nullptr;
+  if (align != (a->num_computed_tokens != nullptr))
+    return fail(KDA_E_ARG, "KDA RecoverSSM align metadata is incomplete");
+  if (align) {
+    if (a->mamba_block_size < a->spec_query_len)
+      return fail(KDA_E_ARG,
+                  "KDA RecoverSSM align block size must cover one "
+                  "speculative window");
+    if (a->block_table_width < 1)
+      return fail(KDA_E_SHAPE, "the block table needs at least one column");
+    if (a->block_table_strides[0] < 0 || a->block_table_strides[1] < 0)
+      return fail(KDA_E_LAYOUT, "block table strides must be non-negative");
+    if (!aligned(a->block_table, 4) || !aligned(a->num_computed_tokens, 4))
+      return fail(KDA_E_UNALIGNED, "align metadata must be 4-byte aligned");
+  }
+  if (a->batch > 0) {
+    if (!a->num_accepted_tokens || !a->state_indices || !a->query_start_loc)
+      return fail(KDA_E_ARG,
+                  "num_accepted_tokens, state_indices and query_start_loc "
+                  "are required");
+    if (!a->commit_lens || !a->final_state_indices ||
+        !a->boundary_state_indices || !a->boundary_recovery_lens)
+      return fail(KDA_E_ARG, "the four plan outputs are required");
+    if (a->num_request_rows < 0 ||
+        (!a->request_indices && a->num_request_rows < a->batch))
+      return fail(KDA_E_ARG,
+                  "KDA RecoverSSM request mapping is too short (%d rows for "
+                  "%d requests)", a->num_request_rows, a->batch);
+    const void* ptrs[] = {a->num_accepted_tokens, a->request_indices,
+                          a->state_indices, a->query_start_loc,
+                          a->commit_lens, a->final_state_indices,
+                          a->boundary_state_indices,
+                          a->boundary_recovery_lens};
+    for (const void* q : ptrs)
+      if (q && !aligned(q, 4))
+        return fail(KDA_E_UNALIGNED, "plan arrays must be 4-byte aligned");
+  }
+  *p = kda::PlanParams{};
+  p->accepted = a->num_accepted_tokens;
+  p->req_idx = a->request_indices;
+  p->slots = a->state_indices;
+  p->qsl = a->query_start_loc;
+  p->table = a->block_table;
+  p->s_tab_row = a->block_table_strides[0];
+  p->s_tab_col = a->block_table_strides[1];
+  p->computed = a->num_computed_tokens;
+  p->lens = a->commit_lens;
+  p->final_slots = a->final_state_indices;
+  p->bnd_slots = a->boundary_state_indices;
+  p->bnd_lens = a->boundary_recovery_lens;
+  p->B = a->batch;
+  p->Q = a->spec_query_len;
+  p->null_id = a->null_block_id;
+  p->block = align ? a->mamba_block_size : 1;
+  p->rows = a->request_indices ? a->num_request_rows : a->batch;
+  p->width = align ? a->block_table_width : 1;
+  return KDA_OK;
+}
+
+// Conv compaction (ops page `KDARecoverSSMCommitContext.create`: matching
+// conv states in every layer, history = length - Q + 1).
+int plan_compact(const kda_compact_args* a, kda::CompactParams* p,
+                 int* elem_bytes) {
+  if (a == nullptr) return fail(KDA_E_ARG, "compaction arguments are NULL");
+  if (a->batch < 0) return fail(KDA_E_ARG, "batch is negative");
+  if (a->num_layers < 1)
+    return fail(KDA_E_ARG, "KDA RecoverSSM commit requires at least one "
+                           "layer");
+  if (a->spec_query_len < 1 || a->spec_query_len > kda::kMaxWindow)
+    return fail(KDA_E_UNSUPPORTED,
+                "KDA RecoverSSM supports windows of 1 to %d",
+                kda::kMaxWindow);
+  if (a->num_slots < 1 || a->conv_dim < 1 || a->conv_dim > 0x7fffffff)
+    return fail(KDA_E_SHAPE, "the conv state pool needs slots and channels");
+  const int e = elem_size(a->conv_dtype);
+  if (e == 0) return fail(KDA_E_DTYPE, "conv state dtype must be F32 or BF16");
+  if (!a->conv_tables)
+    return fail(KDA_E_ARG, "the per-layer conv tables are required");
+  if (!a->boundary_state_indices != !a->boundary_recovery_lens)
+    return fail(KDA_E_ARG, "KDA RecoverSSM align metadata is incomplete");
+  if (a->batch > 0 && (!a->state_indices || !a->commit_lens))
+    return fail(KDA_E_ARG, "state_indices and commit_lens are required");
+  if (a->batch > 65535 || a->num_layers > 65535)
+    return fail(KDA_E_UNSUPPORTED,
+                "the compaction grid holds at most 65535 requests and layers");
+  if (a->host_conv_tables) {
+    const int64_t L = a->num_layers;
+    const int64_t* t = a->host_conv_tables;
+    const int64_t Lc = a->spec_query_len + kda::kConvWidth - 2;
+    for (int64_t l = 0; l < L; ++l) {
+      const int64_t base = t[l], ss = t[L + l], sc = t[2 * L + l],
+                    st = t[3 * L + l];
+      if (base == 0 || base % e != 0)
+        return fail(KDA_E_LAYOUT, "layer %lld: conv state base is not "
+                                  "element aligned", (long long)l);
+      if (ss < 0 || sc < 0 || st < 0)
+        return fail(KDA_E_LAYOUT, "layer %lld: negative conv state stride",
+                    (long long)l);
+      // the last element every channel can touch stays inside its slot
+      if ((a->conv_dim - 1) * sc + (Lc - 1) * st >= ss && a->num_slots > 1)
+        return fail(KDA_E_LAYOUT, "layer %lld: conv state slots overlap",
+                    (long long)l);
+    }
+  }
+  *p = kda::CompactParams{};
+  p->tables = a->conv_tables;
+  p->slots = a->state_indices;
+  p->commit_lens = a->commit_lens;
+  p->final_slots = a->final_state_indices;
+  p->bnd_slots = a->boundary_state_indices;
+  p->bnd_lens = a->boundary_recovery_lens;
+  p->L = a->num_layers;
+  p->B = a->batch;
+  p->Q = a->spec_query_len;
+  p->null_id = a->null_block_id;
+  p->N = a->num_slots;
+  p->C = int32_t(a->conv_dim);
+  *elem_bytes = e;
   return KDA_OK;
 }
 
@@ -556,6 +692,40 @@ int kda_recoverssm_commit(const kda_commit_args* args, void* stream) {
   return device_status(
       kda::launch_commit(plan.p, plan.D, static_cast<hipStream_t>(stream)),
       "kda_recoverssm_commit launch");
+}
+
+int kda_check_commit_plan(const kda_plan_args* args) {
+  g_err.clear();
+  kda::PlanParams p;
+  return plan_plan(args, &p);
+}
+
+int kda_commit_plan(const kda_plan_args* args, void* stream) {
+  g_err.clear();
+  kda::PlanParams p;
+  KDA_TRY(plan_plan(args, &p));
+  if (p.B == 0) return KDA_OK;
+  return device_status(
+      kda::launch_commit_plan(p, static_cast<hipStream_t>(stream)),
+      "kda_commit_plan launch");
+}
+
+int kda_check_compact_conv(const kda_compact_args* args) {
+  g_err.clear();
+  kda::CompactParams p;
+  int e = 0;
+  return plan_compact(args, &p, &e);
+}
+
+int kda_compact_conv_state(const kda_compact_args* args, void* stream) {
+  g_err.clear();
+  kda::CompactParams p;
+  int e = 0;
+  KDA_TRY(plan_compact(args, &p, &e));
+  if (p.B == 0) return KDA_OK;
+  return device_status(
+      kda::launch_compact(p, e, static_cast<hipStream_t>(stream)),
+      "kda_compact_conv_state launch");
 }
 
 int kda_reset_counter(int32_t* counter, int32_t n, void* stream) {

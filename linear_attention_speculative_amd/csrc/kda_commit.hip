@@ -13,6 +13,13 @@
 // streaming read-modify-write of the 64 KiB tile: 16-byte non-temporal
 // loads issued after the small record loads, stores to the final slot.
 //
+// Align mode (prefix caching; ops page `_commit_kda_state_kernel` with
+// ALIGN_MODE): a request may also store the state after its first m
+// positions at a boundary slot,
+//   S_m = S_0 diag(Gam_m) + sum_{t<m} c_t (k_hat_t * Suf^m_t)^T,
+// built from the same tile in registers with a second set of column vectors
+// (a separate instantiation, so the plain commit carries none of it).
+//
 // Schedules: by default one workgroup per (head, request, layer) on a 3-D
 // grid (heads fastest, so consecutive workgroups stream consecutive heads of
 // one slot); with grid > 0, a persistent grid of that many workgroups walks
@@ -36,21 +43,30 @@ struct CommitCfg {
   static_assert(RPP * PASSES == D, "tile rows");
 };
 
+template <int D, int QMAX, bool ALIGN>
+struct BoundarySmem {
+  float wb[QMAX][D];       // k_hat_t * Suf^m_t (0 for t >= m)
+  float gamb[D];           // Gam_m
+};
 template <int D, int QMAX>
+struct BoundarySmem<D, QMAX, false> {};
+
+template <int D, int QMAX, bool ALIGN>
 struct alignas(16) CommitSmem {
   using C = CommitCfg<D, QMAX>;
   float w[QMAX][D];        // k_hat_t * Suf_t
   float gam[D];            // Gam
   float cT[D * C::CS];     // corrections, row v: c_0..c_{Q-1}
   float red[C::CW][QMAX];  // wave partial sums of |k_t|^2
+  BoundarySmem<D, QMAX, ALIGN> bd;
 };
 
 // Commit of one (layer, request, head).  Returns whether it used LDS (a
 // skipped item returns before touching it).
-template <int D, int QMAX>
+template <int D, int QMAX, bool ALIGN>
 __device__ __forceinline__ bool commit_item(const CommitParams& p,
-                                            CommitSmem<D, QMAX>& sm, int l,
-                                            int b, int h) {
+                                            CommitSmem<D, QMAX, ALIGN>& sm,
+                                            int l, int b, int h) {
   using C = CommitCfg<D, QMAX>;
   const int tid = threadIdx.x;
   const int slot = p.slots[b];
@@ -61,11 +77,20 @@ __device__ __forceinline__ bool commit_item(const CommitParams& p,
   if (f <= p.null_id || f < 0 || f >= p.N) return false;
   const int r = p.record_rows ? p.record_rows[b] : slot;
   if (r < 0 || r >= p.R) return false;
+  // boundary slot (align mode): -1 when there is none to store
+  int bslot = -1, m = 0;
+  if constexpr (ALIGN) {
+    bslot = p.bnd_slots[b];
+    m = min(max(p.bnd_lens[b], 0), n);
+    if (bslot <= p.null_id || bslot < 0 || bslot >= p.N) bslot = -1;
+  }
 
   float* state = reinterpret_cast<float*>(p.state_base[l]);
   const int64_t sbs = p.state_bs[l];
   const float* src = state + int64_t(slot) * sbs + int64_t(h) * p.s_state_head;
   float* dst = state + int64_t(f) * sbs + int64_t(h) * p.s_state_head;
+  float* bdst = state + int64_t(bslot < 0 ? f : bslot) * sbs +
+                int64_t(h) * p.s_state_head;
 
   // Records of this head.
   const float* corr = reinterpret_cast<const float*>(p.corr_base[l]) +
@@ -138,16 +163,22 @@ __device__ __forceinline__ bool commit_item(const CommitParams& p,
   lds_barrier();
 
   if (col_ok) {
-    float suf = 1.0f;
+    float suf = 1.0f, sufb = 1.0f;
 #pragma unroll
     for (int t = QMAX - 1; t >= 0; --t) {
       float sk = 0.0f;
 #pragma unroll
       for (int w = 0; w < C::CW; ++w) sk += sm.red[w][t];
-      sm.w[t][tid] = kr[t] * rsqrtf(sk + kNormEps) * suf;
+      const float kh = kr[t] * rsqrtf(sk + kNormEps);
+      sm.w[t][tid] = kh * suf;
       suf *= dd[t];
+      if constexpr (ALIGN) {
+        sm.bd.wb[t][tid] = t < m ? kh * sufb : 0.0f;
+        if (t < m) sufb *= dd[t];
+      }
     }
     sm.gam[tid] = suf;
+    if constexpr (ALIGN) sm.bd.gamb[tid] = sufb;
   }
   lds_barrier();
 
@@ -161,6 +192,24 @@ __device__ __forceinline__ bool commit_item(const CommitParams& p,
     const int row = pp * C::RPP + rg;
     f4 acc = st[pp] * g4;
     const float* cr = &sm.cT[row * C::CS];
+    if constexpr (ALIGN) {
+      // the boundary state first, from the same tile
+      if (bslot >= 0) {
+        f4 bacc = st[pp] * *reinterpret_cast<const f4*>(&sm.bd.gamb[col]);
+#pragma unroll
+        for (int t = 0; t < QMAX; ++t) {
+          if (t < m) {
+            const float c = cr[t];
+            const f4 wb = *reinterpret_cast<const f4*>(&sm.bd.wb[t][col]);
+            bacc.x = fmaf(c, wb.x, bacc.x);
+            bacc.y = fmaf(c, wb.y, bacc.y);
+            bacc.z = fmaf(c, wb.z, bacc.z);
+            bacc.w = fmaf(c, wb.w, bacc.w);
+          }
+        }
+        st_stream(bdst + row * D + col, bacc);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < QMAX; ++t) {
       if (t < n) {
@@ -177,20 +226,20 @@ __device__ __forceinline__ bool commit_item(const CommitParams& p,
 }
 
 // One workgroup per item: blockIdx = (head, request, layer).
-template <int D, int QMAX>
+template <int D, int QMAX, bool ALIGN>
 __global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
     kda_commit_grid_kernel(CommitParams p) {
-  __shared__ CommitSmem<D, QMAX> sm;
-  commit_item<D, QMAX>(p, sm, int(blockIdx.z), int(blockIdx.y),
-                       int(blockIdx.x));
+  __shared__ CommitSmem<D, QMAX, ALIGN> sm;
+  commit_item<D, QMAX, ALIGN>(p, sm, int(blockIdx.z), int(blockIdx.y),
+                              int(blockIdx.x));
 }
 
 // Persistent grid: workgroup g takes items g, g + gridDim.x, ... in
 // (layer, request, head) order, heads fastest.
-template <int D, int QMAX>
+template <int D, int QMAX, bool ALIGN>
 __global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
     kda_commit_strided_kernel(CommitParams p) {
-  __shared__ CommitSmem<D, QMAX> sm;
+  __shared__ CommitSmem<D, QMAX, ALIGN> sm;
   const int per_layer = p.B * p.H;
   const int n_items = p.L * per_layer;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -199,25 +248,31 @@ __global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
     const int b = uniform(rem / p.H);
     const int h = uniform(rem - b * p.H);
     // LDS is reused by the next item: wait until every thread is done.
-    if (commit_item<D, QMAX>(p, sm, l, b, h)) lds_barrier();
+    if (commit_item<D, QMAX, ALIGN>(p, sm, l, b, h)) lds_barrier();
   }
 }
 
-template <int D, int QMAX>
-int launch_cq(const CommitParams& p, hipStream_t stream) {
+template <int D, int QMAX, bool ALIGN>
+int launch_cqa(const CommitParams& p, hipStream_t stream) {
   using C = CommitCfg<D, QMAX>;
   const int64_t items = int64_t(p.L) * p.B * p.H;
   if (items > 0x7fffffff) return int(hipErrorInvalidValue);
   if (p.grid <= 0 && p.B <= 65535 && p.L <= 65535) {
-    hipLaunchKernelGGL((kda_commit_grid_kernel<D, QMAX>),
+    hipLaunchKernelGGL((kda_commit_grid_kernel<D, QMAX, ALIGN>),
                        dim3(p.H, p.B, p.L), dim3(C::NT), 0, stream, p);
   } else {
     const int64_t g = p.grid > 0 ? p.grid : 4096;
-    hipLaunchKernelGGL((kda_commit_strided_kernel<D, QMAX>),
+    hipLaunchKernelGGL((kda_commit_strided_kernel<D, QMAX, ALIGN>),
                        dim3(unsigned(g < items ? g : items)), dim3(C::NT), 0,
                        stream, p);
   }
   return int(hipGetLastError());
+}
+
+template <int D, int QMAX>
+int launch_cq(const CommitParams& p, hipStream_t stream) {
+  return p.bnd_slots ? launch_cqa<D, QMAX, true>(p, stream)
+                     : launch_cqa<D, QMAX, false>(p, stream);
 }
 
 template <int D>

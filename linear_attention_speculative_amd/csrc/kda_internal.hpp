@@ -70,10 +70,41 @@ struct CommitParams {
   const int32_t* commit_lens;
   const int32_t* final_slots;   // may be null
   const int32_t* record_rows;   // may be null
+  const int32_t* bnd_slots;     // align mode (both given) or null
+  const int32_t* bnd_lens;
   int32_t L, B, H, Q, null_id;
   int64_t N, R;
   int32_t kg_bf16;
   int32_t grid;   // <= 0: one workgroup per item; > 0: persistent, strided
+};
+
+// Commit plan: one thread per request.
+struct PlanParams {
+  const int32_t* accepted;   // per request row
+  const int32_t* req_idx;    // [B] or null (row = b)
+  const int32_t* slots;      // [B]
+  const int32_t* qsl;        // [B + 1]
+  const int32_t* table;      // align mode, or null
+  int64_t s_tab_row, s_tab_col;
+  const int32_t* computed;   // per request row (align mode)
+  int32_t* lens;
+  int32_t* final_slots;
+  int32_t* bnd_slots;
+  int32_t* bnd_lens;
+  int32_t B, Q, null_id, block, rows, width;
+};
+
+// Conv-state compaction: one thread per (layer, request, channel).
+struct CompactParams {
+  const int64_t* tables;     // [4][L]: base, slot, channel, token strides
+  const int32_t* slots;
+  const int32_t* commit_lens;
+  const int32_t* final_slots;  // may be null (in place)
+  const int32_t* bnd_slots;    // may be null
+  const int32_t* bnd_lens;
+  int32_t L, B, Q, null_id;
+  int64_t N;
+  int32_t C;                 // channels
 };
 
 // Verify schedules (kda_schedule of the public header).
@@ -86,6 +117,8 @@ constexpr int kScheduleTickets = 2;
 int launch_verify(const VerifyParams& p, int D, bool act_bf16, int schedule,
                   int grid, hipStream_t stream);
 int launch_commit(const CommitParams& p, int D, hipStream_t stream);
+int launch_commit_plan(const PlanParams& p, hipStream_t stream);
+int launch_compact(const CompactParams& p, int elem_bytes, hipStream_t stream);
 int launch_reset_counter(int32_t* counter, int n, hipStream_t stream);
 
 }  // namespace kda

@@ -179,9 +179,11 @@ class CommitContext:
 
     `layers` is a sequence of dicts with `state` [N,H,D,D] f32,
     `correction` [R,H,Q,D] f32, `key_gate` [R,H,Q,2D], `A_log` [H],
-    `dt_bias` [H,D] (or [H*D]) and `lower_bound` (None = softplus).
-    Every layer must share sizes, dtypes and inner strides; slot strides
-    may differ per layer.
+    `dt_bias` [H,D] (or [H*D]) and `lower_bound` (None = softplus), and
+    optionally `conv_state`, the layer's conv state seen dim-first
+    [N, 3HD, Q+2] (a token-first state's `.transpose(1, 2)`), which enables
+    the compaction.  Every layer must share sizes, dtypes and inner
+    strides; slot strides may differ per layer.
     """
 
     def __init__(self, layers: Sequence[dict], *, spec_query_len: int,
@@ -254,9 +256,32 @@ class CommitContext:
         self.lower_bound = torch.tensor(
             [0.0 if L.get("lower_bound") is None else float(L["lower_bound"])
              for L in layers], dtype=torch.float32, device=dev)
+        self.conv_tables = None
+        convs = [L.get("conv_state") for L in layers]
+        if any(c is not None for c in convs):
+            if any(c is None for c in convs):
+                raise ValueError("KDA RecoverSSM layers need matching conv "
+                                 "state")
+            c0 = convs[0]
+            for c in convs:
+                if (c.dim() != 3 or c.shape != c0.shape or
+                        c.dtype != c0.dtype or c.shape[0] != N or
+                        c.shape[2] != Q + 2 or c.dtype not in _DT):
+                    raise ValueError("KDA RecoverSSM layers need matching "
+                                     "conv state")
+            self.conv_dim = c0.shape[1]
+            self.conv_dtype = _DT[c0.dtype]
+            self._host_conv_tables = torch.tensor(
+                [[c.data_ptr() for c in convs],
+                 [c.stride(0) for c in convs],
+                 [c.stride(1) for c in convs],
+                 [c.stride(2) for c in convs]], dtype=torch.int64)
+            self.conv_tables = self._host_conv_tables.to(dev)
 
     def args(self, state_indices, commit_lens, final_state_indices=None,
-             record_rows=None, max_workgroups=0) -> _abi.KdaCommitArgs:
+             record_rows=None, max_workgroups=0,
+             boundary_state_indices=None,
+             boundary_recovery_lens=None) -> _abi.KdaCommitArgs:
         a = _abi.KdaCommitArgs()
         a.num_layers = self.num_layers
         a.batch = state_indices.shape[0]
@@ -291,6 +316,8 @@ class CommitContext:
         a.record_rows = _ptr(record_rows)
         a.host_tables = self._host_tables.numpy().ctypes.data_as(
             ctypes.POINTER(ctypes.c_int64))
+        a.boundary_state_indices = _ptr(boundary_state_indices)
+        a.boundary_recovery_lens = _ptr(boundary_recovery_lens)
         return a
 
     def check(self, state_indices, commit_lens, final_state_indices=None,
@@ -300,13 +327,137 @@ class CommitContext:
         return _abi.load().kda_check_commit(ctypes.byref(a))
 
     def commit(self, state_indices, commit_lens, final_state_indices=None,
-               record_rows=None, stream=None, max_workgroups=0) -> None:
+               record_rows=None, stream=None, max_workgroups=0,
+               boundary_state_indices=None,
+               boundary_recovery_lens=None) -> None:
         """Fold the first commit_lens[b] recorded positions of every request
-        into its checkpoint (or final slot), for all layers, in one launch.
+        into its checkpoint (or final slot), for all layers, in one launch;
+        with boundary slots and lengths (align mode), also store the state
+        after the first boundary_recovery_lens[b] positions there.
         max_workgroups > 0 selects the persistent strided schedule."""
         a = self.args(state_indices, commit_lens, final_state_indices,
-                      record_rows, max_workgroups)
+                      record_rows, max_workgroups, boundary_state_indices,
+                      boundary_recovery_lens)
         rc = _abi.load().kda_recoverssm_commit(ctypes.byref(a),
                                               _stream(stream))
         if rc != _abi.KDA_OK:
             _raise(rc)
+
+    # ---- commit plan and conv compaction -----------------------------------
+
+    def plan_args(self, num_accepted_tokens, state_indices, query_start_loc,
+                  request_indices=None, block_table=None,
+                  num_computed_tokens=None, mamba_block_size=None,
+                  out=None) -> tuple:
+        """Arguments of kda_commit_plan and its four int32 [batch] outputs
+        (allocated on the device of `state_indices` unless `out` is
+        given)."""
+        B = state_indices.shape[0]
+        if out is None:
+            out = tuple(torch.empty(B, dtype=torch.int32,
+                                    device=state_indices.device)
+                        for _ in range(4))
+        a = _abi.KdaPlanArgs()
+        a.batch = B
+        a.spec_query_len = self.Q
+        a.null_block_id = self.null_block_id
+        a.mamba_block_size = mamba_block_size or 0
+        rows = [num_accepted_tokens.shape[0]]
+        if block_table is not None:
+            if block_table.dim() != 2:
+                raise ValueError("KDA RecoverSSM block table must be "
+                                 "two-dimensional")
+            if block_table.dtype != torch.int32:
+                raise TypeError("the block table must be int32")
+            rows.append(block_table.shape[0])
+            a.block_table = block_table.data_ptr()
+            a.block_table_width = block_table.shape[1]
+            a.block_table_strides[:] = list(block_table.stride())
+        if num_computed_tokens is not None:
+            rows.append(num_computed_tokens.shape[0])
+        a.num_request_rows = min(rows)
+        if request_indices is not None and request_indices.shape[0] < B:
+            raise ValueError("KDA RecoverSSM request mapping is too short")
+        a.num_accepted_tokens = _ptr(num_accepted_tokens)
+        a.request_indices = _ptr(request_indices)
+        a.state_indices = _ptr(state_indices)
+        a.query_start_loc = _ptr(query_start_loc)
+        a.num_computed_tokens = _ptr(num_computed_tokens)
+        a.commit_lens, a.final_state_indices, a.boundary_state_indices, \
+            a.boundary_recovery_lens = (_ptr(t) for t in out)
+        return a, out
+
+    def plan(self, num_accepted_tokens, state_indices, query_start_loc,
+             request_indices=None, block_table=None, num_computed_tokens=None,
+             mamba_block_size=None, out=None, stream=None) -> tuple:
+        """The commit plan (ops page `_prepare_commit_plan_kernel`): returns
+        (commit_lens, final_state_indices, boundary_state_indices,
+        boundary_recovery_lens), int32 [batch] on the device.  With a block
+        table, num_computed_tokens and mamba_block_size (align mode) the
+        final slot is the block of the next token and a completed block
+        gets the boundary state."""
+        a, out = self.plan_args(num_accepted_tokens, state_indices,
+                                query_start_loc, request_indices, block_table,
+                                num_computed_tokens, mamba_block_size, out)
+        rc = _abi.load().kda_commit_plan(ctypes.byref(a), _stream(stream))
+        if rc != _abi.KDA_OK:
+            _raise(rc)
+        return out
+
+    def compact_args(self, state_indices, commit_lens,
+                     final_state_indices=None, boundary_state_indices=None,
+                     boundary_recovery_lens=None) -> _abi.KdaCompactArgs:
+        if self.conv_tables is None:
+            raise ValueError("this commit context has no conv states")
+        a = _abi.KdaCompactArgs()
+        a.num_layers = self.num_layers
+        a.batch = state_indices.shape[0]
+        a.spec_query_len = self.Q
+        a.null_block_id = self.null_block_id
+        a.num_slots = self.N
+        a.conv_dim = self.conv_dim
+        a.conv_dtype = self.conv_dtype
+        a.conv_tables = self.conv_tables.data_ptr()
+        a.host_conv_tables = self._host_conv_tables.numpy().ctypes.data_as(
+            ctypes.POINTER(ctypes.c_int64))
+        a.state_indices = _ptr(state_indices)
+        a.commit_lens = _ptr(commit_lens)
+        a.final_state_indices = _ptr(final_state_indices)
+        a.boundary_state_indices = _ptr(boundary_state_indices)
+        a.boundary_recovery_lens = _ptr(boundary_recovery_lens)
+        return a
+
+    def compact(self, state_indices, commit_lens, final_state_indices=None,
+                boundary_state_indices=None, boundary_recovery_lens=None,
+                stream=None) -> None:
+        """Conv-state compaction of every layer (ops page
+        `_compact_conv_state_kernel`): the three inputs before token n of
+        each committing request's window go to the front of its final (and,
+        in align mode, boundary) slot's conv state."""
+        a = self.compact_args(state_indices, commit_lens, final_state_indices,
+                              boundary_state_indices, boundary_recovery_lens)
+        rc = _abi.load().kda_compact_conv_state(ctypes.byref(a),
+                                               _stream(stream))
+        if rc != _abi.KDA_OK:
+            _raise(rc)
+
+    def commit_step(self, num_accepted_tokens, state_indices, query_start_loc,
+                    request_indices=None, block_table=None,
+                    num_computed_tokens=None, mamba_block_size=None,
+                    record_rows=None, stream=None) -> tuple:
+        """The ops page's `KDARecoverSSMCommitContext.commit`: plan, conv
+        compaction (when the context has conv states), then the state
+        commit of every layer.  Returns the plan's four arrays."""
+        align = block_table is not None
+        lens, final, bnd, blens = self.plan(
+            num_accepted_tokens, state_indices, query_start_loc,
+            request_indices, block_table, num_computed_tokens,
+            mamba_block_size, stream=stream)
+        if self.conv_tables is not None:
+            self.compact(state_indices, lens, final,
+                         bnd if align else None, blens if align else None,
+                         stream=stream)
+        self.commit(state_indices, lens, final, record_rows, stream=stream,
+                    boundary_state_indices=bnd if align else None,
+                    boundary_recovery_lens=blens if align else None)
+        return lens, final, bnd, blens

@@ -364,7 +364,8 @@ def commit_plan(*, num_accepted_tokens, state_indices, query_start_loc,
 
     Row b of the batch reads its per-request values (accepted count, block
     table row, computed-token count) at row request_indices[b] (default b);
-    its state slot and window at b.  Then
+    its state slot and window at b.  A row outside those arrays plans no
+    commit (n = 0, final = source, no boundary).  Then
       n = accepted count clamped to [0, q_b]   (0 for a null slot);
     without a block table: final = source slot, no boundary;
     with one (prefix caching, one state block per `mamba_block_size` = bs
@@ -375,7 +376,8 @@ def commit_plan(*, num_accepted_tokens, state_indices, query_start_loc,
       if that block starts at P with c < P <= end, the committed tokens
       completed the block before it: boundary = block_table[row, P/bs - 1]
       receives the state after its last token, i.e. after P - c positions
-      (all n of them when P = end: then both blocks get the same state).
+      (all n of them when P = end: then both blocks get the same state);
+      a boundary block past the table's width is null (length 0).
     Since bs >= Q, one window completes at most one block.  The running
     block is always the incomplete one, so the verify's in-place conv roll
     (at the source, the block of token c) never touches a completed block.
@@ -384,12 +386,20 @@ def commit_plan(*, num_accepted_tokens, state_indices, query_start_loc,
     Q = int(spec_query_len)
     B = len(state_indices)
     qsl = np.asarray(query_start_loc)
+    # rows of the per-request arrays; a row outside them commits nothing
+    rows = len(num_accepted_tokens)
+    if block_table is not None:
+        rows = min(rows, len(block_table), len(num_computed_tokens))
+    if request_indices is None:
+        rows = max(rows, B)
     lens = np.zeros(B, dtype=np.int64)
     final = np.array(state_indices, dtype=np.int64, copy=True)
     boundary = np.full(B, null_block_id, dtype=np.int64)
     blens = np.zeros(B, dtype=np.int64)
     for b in range(B):
         row = b if request_indices is None else int(request_indices[b])
+        if not 0 <= row < rows:
+            continue
         q = min(max(int(qsl[b + 1]) - int(qsl[b]), 0), Q)
         n = min(max(int(num_accepted_tokens[row]), 0), q)
         if int(state_indices[b]) <= null_block_id:
@@ -404,7 +414,7 @@ def commit_plan(*, num_accepted_tokens, state_indices, query_start_loc,
         final[b] = int(block_table[row][last]) if last < width \
             else null_block_id
         start = last * bs
-        if c < start:
+        if c < start and last - 1 < width:
             boundary[b] = int(block_table[row][last - 1])
             blens[b] = start - c
     return lens, final, boundary, blens

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_abi.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert kda.abi_version() == 2
+    assert kda.abi_version() == 3
     assert lib.kda_status_string(_abi.KDA_E_UNALIGNED) == b"KDA_E_UNALIGNED"
 
 
@@ -281,3 +281,99 @@ def test_commit_abi_codes():
         a.host_tables = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
     assert code(mis) == _abi.KDA_E_LAYOUT
     assert b"layer 1" in lib.kda_last_error()
+
+
+# ---- commit plan, conv compaction, align-mode commit ---------------------------
+
+def _align_ctx():
+    wl = make_workload("ragged", B=6, H=2, D=16, Q=4, N=12, act="bf16",
+                       weight="bf16")
+    layers = [dict(state=L.state, correction=L.correction,
+                   key_gate=L.key_gate, A_log=L.A_log, dt_bias=L.dt_bias,
+                   lower_bound=L.lower_bound if L.use_lower_bound else None,
+                   conv_state=wl.conv_state_dim_first(i))
+              for i, L in enumerate(wl.layers)]
+    return wl, kda.CommitContext(layers, spec_query_len=wl.Q)
+
+
+def test_plan_checks():
+    wl, ctx = _align_ctx()
+    lib = kda.load()
+    acc = wl.num_accepted_tokens
+    table = torch.zeros(wl.B, 5, dtype=torch.int32)
+    computed = torch.zeros(wl.B, dtype=torch.int32)
+
+    def code(**kw):
+        base = dict(num_accepted_tokens=acc, state_indices=wl.state_indices,
+                    query_start_loc=wl.query_start_loc)
+        base.update(kw)
+        a, _ = ctx.plan_args(**base)
+        return lib.kda_check_commit_plan(ctypes.byref(a))
+
+    assert code() == 0
+    assert code(block_table=table, num_computed_tokens=computed,
+                mamba_block_size=4) == 0
+    # align arguments all or none
+    assert code(block_table=table, mamba_block_size=4) == _abi.KDA_E_ARG
+    assert code(num_computed_tokens=computed) == _abi.KDA_E_ARG
+    # a block must cover one window
+    assert code(block_table=table, num_computed_tokens=computed,
+                mamba_block_size=3) == _abi.KDA_E_ARG
+    a, _ = ctx.plan_args(num_accepted_tokens=acc,
+                         state_indices=wl.state_indices,
+                         query_start_loc=wl.query_start_loc,
+                         block_table=table, num_computed_tokens=computed,
+                         mamba_block_size=4)
+    a.block_table_width = 0
+    assert lib.kda_check_commit_plan(ctypes.byref(a)) == _abi.KDA_E_SHAPE
+    # too few request rows for an identity mapping
+    assert code(num_accepted_tokens=acc[:-1]) == _abi.KDA_E_ARG
+    # with a mapping, the rows may be fewer or more than the batch
+    assert code(num_accepted_tokens=acc[:2],
+                request_indices=torch.zeros(wl.B, dtype=torch.int32)) == 0
+    with pytest.raises(ValueError):
+        ctx.plan_args(num_accepted_tokens=acc, state_indices=wl.state_indices,
+                      query_start_loc=wl.query_start_loc,
+                      request_indices=torch.zeros(wl.B - 1,
+                                                  dtype=torch.int32))
+    with pytest.raises(ValueError):
+        ctx.plan_args(num_accepted_tokens=acc, state_indices=wl.state_indices,
+                      query_start_loc=wl.query_start_loc,
+                      block_table=table[0], num_computed_tokens=computed,
+                      mamba_block_size=4)
+
+
+def test_compaction_and_boundary_checks():
+    wl, ctx = _align_ctx()
+    lib = kda.load()
+    si, lens = wl.state_indices, wl.commit_lens
+    a = ctx.compact_args(si, lens)
+    assert lib.kda_check_compact_conv(ctypes.byref(a)) == 0
+    a = ctx.compact_args(si, lens, si, si, None)
+    assert lib.kda_check_compact_conv(ctypes.byref(a)) == _abi.KDA_E_ARG
+    a = ctx.compact_args(si, lens)
+    a.conv_dtype = 9
+    assert lib.kda_check_compact_conv(ctypes.byref(a)) == _abi.KDA_E_DTYPE
+    a = ctx.compact_args(si, lens)
+    a.num_layers = 0
+    assert lib.kda_check_compact_conv(ctypes.byref(a)) == _abi.KDA_E_ARG
+    # slots that would overlap in the host copy of the tables
+    host = ctx._host_conv_tables.clone()
+    host[1, 0] = 8
+    keep = host.numpy()
+    a = ctx.compact_args(si, lens)
+    a.host_conv_tables = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    assert lib.kda_check_compact_conv(ctypes.byref(a)) == _abi.KDA_E_LAYOUT
+    # the commit: boundary slots and lengths go together
+    assert lib.kda_check_commit(ctypes.byref(ctx.args(si, lens))) == 0
+    a = ctx.args(si, lens, boundary_state_indices=si)
+    assert lib.kda_check_commit(ctypes.byref(a)) == _abi.KDA_E_ARG
+    a = ctx.args(si, lens, boundary_state_indices=si,
+                 boundary_recovery_lens=lens)
+    assert lib.kda_check_commit(ctypes.byref(a)) == 0
+    # a context without conv states cannot compact
+    plain = kda.CommitContext([{k: v for k, v in L.items()
+                                if k != "conv_state"} for L in ctx.layers],
+                              spec_query_len=wl.Q)
+    with pytest.raises(ValueError):
+        plain.compact_args(si, lens)

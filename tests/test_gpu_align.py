@@ -1,0 +1,247 @@
+"""Parity of the HIP commit plan, conv compaction and align-mode commit
+(called through the C ABI) with the fp64 oracle: the plan and the compaction
+bit for bit, the boundary and final states to the commit's tolerance, and a
+multi-step prefix-caching sequence (verify -> plan -> compaction -> commit)
+checked against the oracle at every step."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_speculative_amd as kda
+import oracle
+from tests.gpu_check import TOL, bits, f64, rel_err
+from workloads import drive, make_workload
+from workloads.gen import block_tables, step_activations
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _i32(a):
+    return torch.as_tensor(np.asarray(a), dtype=torch.int32, device=DEV)
+
+
+def _np(t):
+    return t.cpu().numpy().astype(np.int64)
+
+
+def _destinations(rng, sources, N):
+    """Final and boundary slots that never collide with another request's
+    source or destination: each is the request's own source, a fresh free
+    slot, or null (boundary only)."""
+    free = [s for s in range(1, N) if s not in set(sources.tolist())]
+    rng.shuffle(free)
+    final, bnd = [], []
+    for s in sources:
+        final.append(int(s) if rng.random() < 0.4 else free.pop())
+        r = rng.random()
+        bnd.append(0 if r < 0.3 else (int(s) if r < 0.5 else free.pop()))
+    return np.array(final), np.array(bnd)
+
+
+# ---- the plan ------------------------------------------------------------------
+
+@pytest.mark.parametrize("align,mapped", [(False, False), (False, True),
+                                          (True, False), (True, True)])
+def test_plan_matches_oracle_bitwise(align, mapped):
+    rng = np.random.default_rng(40 + 2 * align + mapped)
+    wl = make_workload("ragged", DEV, B=4, H=2, D=16, Q=4, N=8)
+    ctx = drive.commit_context(wl)
+    B, Q, bs, width = 300, wl.Q, 6, 9
+    rows = B + 7 if mapped else B
+    acc = rng.integers(-1, Q + 3, size=rows)
+    req = rng.permutation(rows)[:B]
+    if mapped:
+        req[:5] = [rows, rows + 3, -1, -2, rows - 1]   # rows out of range
+    slots = rng.integers(0, 60, size=B)
+    qlen = rng.integers(0, Q + 1, size=B)
+    qsl = np.concatenate([[0], np.cumsum(qlen)])
+    wide = rng.integers(-1, 60, size=(rows, 2 * width))
+    table = wide[:, ::2]                               # a strided view
+    computed = rng.integers(-3, width * bs + 5, size=rows)
+    kw = dict(num_accepted_tokens=_i32(acc), state_indices=_i32(slots),
+              query_start_loc=_i32(qsl),
+              request_indices=_i32(req) if mapped else None)
+    okw = dict(num_accepted_tokens=acc, state_indices=slots,
+               query_start_loc=qsl, spec_query_len=Q,
+               request_indices=req if mapped else None)
+    if align:
+        kw.update(block_table=_i32(wide)[:, ::2],
+                  num_computed_tokens=_i32(computed), mamba_block_size=bs)
+        okw.update(block_table=table, num_computed_tokens=computed,
+                   mamba_block_size=bs)
+    got = ctx.plan(**kw)
+    torch.cuda.synchronize()
+    ref = oracle.commit_plan(**okw)
+    for name, g, r in zip(("lens", "final", "boundary", "blens"), got, ref):
+        assert np.array_equal(_np(g), r), name
+    if align:
+        assert (ref[3] > 0).sum() > 20                 # boundaries occurred
+
+
+# ---- the compaction ------------------------------------------------------------
+
+@pytest.mark.parametrize("dim_first,act", [(True, "bf16"), (False, "f32"),
+                                           (True, "f32"), (False, "bf16")])
+def test_compaction_matches_oracle_bitwise(dim_first, act):
+    rng = np.random.default_rng(50 + dim_first + 2 * (act == "f32"))
+    wl = make_workload("large", DEV, B=24, H=2, D=32, Q=8, N=80, act=act,
+                       weight=act, gates=[None, -5.0, None],
+                       conv_dim_first=dim_first)
+    ctx = drive.commit_context(wl, conv=True)
+    src = _np(wl.state_indices)
+    final, bnd = _destinations(rng, src, wl.N)
+    lens = rng.integers(-1, wl.Q + 2, size=wl.B)
+    blens = rng.integers(-1, wl.Q + 2, size=wl.B)
+    src[3] = 0                                         # a null request
+    si = _i32(src)
+    before = [bits(wl.conv_state_dim_first(l)) for l in range(3)]
+    pages = [L.page.clone() for L in wl.layers]
+    ctx.compact(si, _i32(lens), _i32(final), _i32(bnd), _i32(blens))
+    torch.cuda.synchronize()
+    ref = oracle.compact_conv_state(
+        conv_states=before, state_indices=src, commit_lens=lens,
+        final_state_indices=final, boundary_state_indices=bnd,
+        boundary_recovery_lens=blens)
+    for l in range(3):
+        assert np.array_equal(bits(wl.conv_state_dim_first(l)), ref[l])
+        assert not np.array_equal(ref[l], before[l])
+        # nothing outside the conv views changed
+        L = wl.layers[l]
+        off, n = wl.meta["page_views"]["conv"]
+        keep = torch.ones(L.page.shape[1], dtype=torch.bool, device=DEV)
+        keep[off:off + n] = False
+        assert torch.equal(L.page[:, keep], pages[l][:, keep])
+
+
+# ---- the align-mode commit ---------------------------------------------------------
+
+def test_align_commit_matches_oracle():
+    rng = np.random.default_rng(61)
+    wl = make_workload("large", DEV, B=24, H=4, D=128, Q=8, N=80,
+                       gates=[None, -5.0, None])
+    for layer in range(3):
+        drive.verify(wl, layer, torch.zeros(1, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    src = _np(wl.state_indices)
+    final, bnd = _destinations(rng, src, wl.N)
+    lens = rng.integers(0, wl.Q + 1, size=wl.B)
+    blens = rng.integers(-1, wl.Q + 2, size=wl.B)
+    lens[:3] = wl.Q
+    blens[:3] = [0, wl.Q, 3]                       # m = 0, m = n, m inside
+    inputs = []
+    for L in wl.layers:
+        inputs.append(dict(state=f64(L.state), correction=f64(L.correction),
+                           key_gate=f64(L.key_gate), A_log=f64(L.A_log),
+                           dt_bias=f64(L.dt_bias),
+                           use_lower_bound=L.use_lower_bound,
+                           lower_bound=L.lower_bound))
+    before = [L.state.clone() for L in wl.layers]
+    ctx = drive.commit_context(wl)
+    ctx.commit(_i32(src), _i32(lens), final_state_indices=_i32(final),
+               boundary_state_indices=_i32(bnd),
+               boundary_recovery_lens=_i32(blens))
+    torch.cuda.synchronize()
+    refs = oracle.commit(layers=inputs, state_indices=src, commit_lens=lens,
+                         spec_query_len=wl.Q, final_state_indices=final,
+                         boundary_state_indices=bnd,
+                         boundary_recovery_lens=blens)
+    n_bnd = 0
+    for l, (new, written) in enumerate(refs):
+        L = wl.layers[l]
+        w = written.any(axis=1)
+        gpu = f64(L.state)
+        err = rel_err(gpu[w], new[w])
+        assert err <= TOL[wl.act], (l, err)
+        keep = torch.as_tensor(~w, device=DEV)
+        assert torch.equal(L.state[keep], before[l][keep])
+        n_bnd += int(sum(1 for b in range(wl.B) if 0 < bnd[b] and
+                         lens[b] > 0 and 0 < final[b] and written[bnd[b]].all()))
+    assert n_bnd > 10
+
+
+# ---- a prefix-caching sequence ----------------------------------------------------
+
+def test_align_sequence_matches_oracle():
+    """Eight requests, each with its own table of state blocks (6 tokens per
+    block), through several speculative steps: verify the running block
+    (accepted count 1: the history was compacted), then plan, compaction
+    and commit of every layer in one call.  At every step, each GPU result
+    equals the oracle run from the same pools."""
+    rng = np.random.default_rng(71)
+    B, H, D, Q, bs, width = 8, 2, 32, 4, 6, 8
+    wl = make_workload("ragged", DEV, B=B, H=H, D=D, Q=Q, N=B * width + 1,
+                       act="bf16", weight="bf16", gates=[None, -5.0])
+    N = wl.N
+    ctx = drive.commit_context(wl, conv=True)
+    tables = block_tables(B, width, N, seed=7)
+    table_t = _i32(tables)
+    c = rng.integers(1, 2 * bs, size=B)
+    tol = TOL["bf16"]
+    crossings = 0
+    for step in range(6):
+        qlen = rng.integers(1, Q + 1, size=B)
+        qsl = np.concatenate([[0], np.cumsum(qlen)])
+        T = int(qsl[-1])
+        acc = np.minimum(rng.integers(1, Q + 1, size=B), qlen)
+        src = tables[np.arange(B), c // bs]
+        meta = dict(query_start_loc=_i32(qsl), state_indices=_i32(src),
+                    num_accepted_tokens=_i32(np.ones(B)))
+        acts = step_activations(T, H, D, "bf16", seed=100 + step, device=DEV)
+        oracle_in, outs = [], []
+        for l, L in enumerate(wl.layers):
+            oracle_in.append(dict(
+                mixed_qkv=f64(acts["mixed_qkv"]), raw_gate=f64(acts["raw_gate"]),
+                raw_beta=f64(acts["raw_beta"]), A_log=f64(L.A_log),
+                dt_bias=f64(L.dt_bias), state=f64(L.state),
+                correction=f64(L.correction), key_gate=f64(L.key_gate),
+                out=np.zeros((T, H * D)),
+                conv_state=f64(wl.conv_state_dim_first(l)),
+                conv_weight=f64(L.conv_weight), query_start_loc=qsl,
+                state_indices=src, num_accepted_tokens=np.ones(B, np.int64),
+                spec_query_len=Q, use_lower_bound=L.use_lower_bound,
+                lower_bound=L.lower_bound))
+            kw = drive.verify_kwargs(wl, l, None, schedule=1)
+            kw.update(acts)
+            kw.update(meta)
+            kw["out"] = torch.zeros(T, H * D, device=DEV)
+            kda.conv_update_verify(**kw)
+            outs.append(kw["out"])
+        plan = ctx.commit_step(_i32(acc), meta["state_indices"],
+                               meta["query_start_loc"], block_table=table_t,
+                               num_computed_tokens=_i32(c),
+                               mamba_block_size=bs)
+        torch.cuda.synchronize()
+        ref_plan = oracle.commit_plan(
+            num_accepted_tokens=acc, state_indices=src, query_start_loc=qsl,
+            spec_query_len=Q, block_table=tables, num_computed_tokens=c,
+            mamba_block_size=bs)
+        for g, r in zip(plan, ref_plan):
+            assert np.array_equal(_np(g), r), step
+        lens, final, bnd, blens = ref_plan
+        crossings += int((bnd > 0).sum())
+        for l, L in enumerate(wl.layers):
+            v = oracle.conv_update_verify(**oracle_in[l])
+            assert rel_err(f64(outs[l]), v["out"]) <= tol
+            conv, = oracle.compact_conv_state(
+                conv_states=[v["conv_state"]], state_indices=src,
+                commit_lens=lens, final_state_indices=final,
+                boundary_state_indices=bnd, boundary_recovery_lens=blens)
+            assert np.array_equal(f64(wl.conv_state_dim_first(l)), conv), \
+                (step, l)
+            (new, written), = oracle.commit(
+                layers=[dict(state=oracle_in[l]["state"],
+                             correction=v["correction"],
+                             key_gate=v["key_gate"], A_log=oracle_in[l]["A_log"],
+                             dt_bias=oracle_in[l]["dt_bias"],
+                             use_lower_bound=L.use_lower_bound,
+                             lower_bound=L.lower_bound)],
+                state_indices=src, commit_lens=lens, spec_query_len=Q,
+                final_state_indices=final, boundary_state_indices=bnd,
+                boundary_recovery_lens=blens)
+            w = written.any(axis=1)
+            gpu = f64(L.state)
+            assert rel_err(gpu[w], new[w]) <= tol, (step, l)
+            assert np.array_equal(gpu[~w], oracle_in[l]["state"][~w])
+        c = c + lens
+    assert crossings >= 4

@@ -66,15 +66,19 @@ def verify_qkv(wl: Workload, layer: int, counter=None, mixed_qkv=None,
         counter, **kw))
 
 
-def commit_context(wl: Workload, layers: Optional[list] = None
-                   ) -> kda.CommitContext:
+def commit_context(wl: Workload, layers: Optional[list] = None,
+                   conv: bool = False) -> kda.CommitContext:
+    """The layers' commit context; `conv` adds their conv states (for the
+    compaction)."""
     idx = range(len(wl.layers)) if layers is None else layers
     return kda.CommitContext(
         [dict(state=wl.layers[i].state, correction=wl.layers[i].correction,
               key_gate=wl.layers[i].key_gate, A_log=wl.layers[i].A_log,
               dt_bias=wl.layers[i].dt_bias,
               lower_bound=wl.layers[i].lower_bound
-              if wl.layers[i].use_lower_bound else None) for i in idx],
+              if wl.layers[i].use_lower_bound else None,
+              **({"conv_state": wl.conv_state_dim_first(i)} if conv else {}))
+         for i in idx],
         spec_query_len=wl.Q, null_block_id=wl.null_block_id)
 
 

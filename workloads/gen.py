@@ -301,3 +301,28 @@ def make_workload(name: str, device="cpu", *, seed: Optional[int] = None,
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact widening of a tensor's values to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def step_activations(T: int, H: int, D: int, act: str, seed: int,
+                     device="cpu") -> dict:
+    """Fresh activations of one decode step: mixed_qkv [T, 3HD], raw_gate
+    [T, HD] and raw_beta [T, H] ~ N(0, 1) in the activation dtype."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 104729 + 3)
+    dt = _TORCH_DTYPE[act]
+    return dict(
+        mixed_qkv=_randn((T, 3 * H * D), 1.0, gen, device).to(dt),
+        raw_gate=_randn((T, H * D), 1.0, gen, device).to(dt),
+        raw_beta=_randn((T, H), 1.0, gen, device).to(dt))
+
+
+def block_tables(B: int, width: int, N: int, seed: int,
+                 null_block_id: int = 0) -> np.ndarray:
+    """Every request's state blocks: int32 [B, width] of distinct live slots
+    drawn without replacement from (null_block_id, N)."""
+    rng = np.random.default_rng(seed)
+    live = np.arange(null_block_id + 1, N)
+    if live.size < B * width:
+        raise ValueError("the pool is too small for the block tables")
+    return rng.permutation(live)[:B * width].reshape(B, width) \
+        .astype(np.int32)
