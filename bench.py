@@ -22,6 +22,17 @@ evicts the caches), so that any help from the last-level cache between
 kernels shows up as a difference; `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload.
 
+Other workloads (`--workload`), each one JSON line of the same form:
+  large     24 layers: 24 verifies, then one commit launch over all layers
+            (B=256, Q=8);
+  deferred  the deferred sequence at scale (B=1024, two layers): per layer
+            one fused launch that folds the previous step's pending records
+            into the checkpoint and then verifies;
+  align     the headline batch under prefix caching (16-token state
+            blocks): verify of the running block, then the commit plan,
+            conv compaction and align-mode commit.
+The default run (headline) is the one the throughput figure is quoted on.
+
   python bench.py [--steps K] [--warmup W] [--workload NAME]
   python bench.py --copy-calibration   # plain copy for HBM counter scaling
 """
@@ -56,10 +67,15 @@ def kernel_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl) -> dict:
+def algorithmic_bytes(wl, pending=None, boundary=None) -> dict:
     """Bytes the method must move per launch (each state tile read once by
     the verify, read and written once by the commit; every activation,
-    record and conv byte once), from the workload's seeded metadata."""
+    record and conv byte once), from the workload's seeded metadata.
+    `pending` (per request): the fused deferred flush also reads that many
+    records and writes the state tile back.  `boundary` (per request, the
+    boundary length or 0): align mode also writes the boundary state, and
+    the compaction moves three conv entries per channel to each of the
+    final and boundary slots."""
     import numpy as np
     H, D, Q, W = wl.H, wl.D, wl.Q, wl.W
     e_act = 2 if wl.act == "bf16" else 4
@@ -73,6 +89,8 @@ def algorithmic_bytes(wl) -> dict:
     per_launch = C * W * e_w + 4 * H + 4 * H * D + 4 * (3 * wl.B + 1)
     verify = per_launch
     commit = 4 * H + 4 * H * D + 8 * wl.B   # gate params, slots + lens
+    flush = 0
+    compact = 0
     tokens = 0
     for b in range(wl.B):
         q = int(min(max(qsl[b + 1] - qsl[b], 0), Q))
@@ -91,7 +109,81 @@ def algorithmic_bytes(wl) -> dict:
         n = int(min(max(lens[b], 0), Q))
         if n > 0:
             commit += 8 * H * D * D + n * (4 * H * D + 2 * H * D * e_kg)
-    return dict(verify=verify, commit=commit, tokens=tokens)
+            if boundary is not None:
+                compact += 2 * (W - 1) * C * e_act
+                if boundary[b] > 0:
+                    commit += 4 * H * D * D
+                    compact += 2 * (W - 1) * C * e_act
+        if pending is not None:
+            m = int(min(max(pending[b], 0), Q))
+            if m > 0:
+                flush += 4 * H * D * D + m * (4 * H * D + 2 * H * D * e_kg)
+    return dict(verify=verify, commit=commit, tokens=tokens, flush=flush,
+                compact=compact)
+
+
+def build_phases(name, wl, drive, torch):
+    """The launches of one step of workload `name`, as phases timed with
+    events on both sides: (kernel, algorithmic bytes per step, launches per
+    step, function).  Returns (phases, verified tokens per step, config
+    note)."""
+    import numpy as np
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L = len(wl.layers)
+    if name == "deferred":
+        nb = algorithmic_bytes(wl, pending=wl.commit_lens.cpu().numpy())
+
+        def fused():
+            for layer in range(L):
+                drive.verify(wl, layer, counter, pending_lens=wl.commit_lens)
+        return ([("kda_verify_grid_kernel", (nb["verify"] + nb["flush"]) * L,
+                  L, fused)], nb["tokens"] * L,
+                f"layers={L} fused flush+verify, pending 0..{wl.Q}")
+    ctx = drive.commit_context(wl, conv=name == "align")
+    if name == "align":
+        bs = 16
+        rng = np.random.default_rng(5)
+        slots = wl.state_indices.cpu().numpy()
+        free = [s for s in range(1, wl.N) if s not in set(slots.tolist())]
+        table = np.zeros((wl.B, 2), dtype=np.int32)
+        table[:, 0] = slots
+        table[:len(free), 1] = free[:wl.B]
+        computed = rng.integers(0, bs, size=wl.B).astype(np.int32)
+        lens = wl.commit_lens.cpu().numpy()
+        boundary = np.where(computed + lens >= bs, bs - computed, 0)
+        nb = algorithmic_bytes(wl, boundary=boundary)
+        table_t = torch.as_tensor(table, device="cuda")
+        computed_t = torch.as_tensor(computed, device="cuda")
+        ones = torch.ones(wl.B, dtype=torch.int32, device="cuda")
+        kw = drive.verify_kwargs(wl, 0, counter)
+        kw["num_accepted_tokens"] = ones
+        from linear_attention_speculative_amd import conv_update_verify
+
+        def verify():
+            conv_update_verify(**kw)
+
+        def commit():
+            ctx.commit_step(wl.commit_lens, wl.state_indices,
+                            wl.query_start_loc, block_table=table_t,
+                            num_computed_tokens=computed_t,
+                            mamba_block_size=bs)
+        return ([("kda_verify_grid_kernel", nb["verify"], 1, verify),
+                 ("commit_step(plan+compaction+commit)",
+                  nb["commit"] + nb["compact"], 1, commit)], nb["tokens"],
+                f"layers=1 align bs={bs}, {int((boundary > 0).sum())} "
+                "boundaries per step")
+    nb = algorithmic_bytes(wl)
+
+    def verify_all():
+        for layer in range(L):
+            drive.verify(wl, layer, counter)
+
+    def commit():
+        ctx.commit(wl.state_indices, wl.commit_lens,
+                   record_rows=wl.record_rows)
+    return ([("kda_verify_grid_kernel", nb["verify"] * L, L, verify_all),
+             ("kda_commit_grid_kernel", nb["commit"] * L, 1, commit)],
+            nb["tokens"] * L, f"layers={L}")
 
 
 def traffic_from_profiles(kernel: str, workload: str):
@@ -191,28 +283,25 @@ def main() -> int:
     from workloads import make_workload
     from workloads import drive
 
-    wl = make_workload(args.workload, "cuda", out_dtype="act")
-    nbytes = algorithmic_bytes(wl)
-    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ctx = drive.commit_context(wl)
+    cfg_name = "headline" if args.workload == "align" else args.workload
+    wl = make_workload(cfg_name, "cuda", out_dtype="act")
+    phases, tokens, note = build_phases(args.workload, wl, drive, torch)
+    P = len(phases)
 
     def step(ev=None):
+        for i, (_, _, _, fn) in enumerate(phases):
+            if ev is not None:
+                ev[i].record()
+            fn()
         if ev is not None:
-            ev[0].record()
-        drive.verify(wl, 0, counter)
-        if ev is not None:
-            ev[1].record()
-        ctx.commit(wl.state_indices, wl.commit_lens,
-                   record_rows=wl.record_rows)
-        if ev is not None:
-            ev[2].record()
+            ev[P].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(P + 1)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -221,67 +310,54 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    v_all = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in events)
-    c_all = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in events)
-    v_ms = sum(v_all) / args.steps / 1e3
-    c_ms = sum(c_all) / args.steps / 1e3
-    print(f"# timed {args.steps} steps: {ms_step:.4f} ms/step (verify "
-          f"{v_ms * 1e3:.1f} us, commit {c_ms * 1e3:.1f} us)",
+    # per phase: microseconds per launch (a phase of n launches / n)
+    per = [sorted(e[i].elapsed_time(e[i + 1]) * 1e3 / phases[i][2]
+                  for e in events) for i in range(P)]
+    mean_ms = [sum(x) / args.steps / 1e3 for x in per]
+    print(f"# timed {args.steps} steps: {ms_step:.4f} ms/step ("
+          + ", ".join(f"{ph[0]} {m * 1e3:.1f} us/launch"
+                      for ph, m in zip(phases, mean_ms)) + ")",
           file=sys.stderr, flush=True)
 
     def quant(xs, q):
         return xs[min(len(xs) - 1, int(q * len(xs)))]
 
-    # Cold launches: each after an untimed 1 GiB write.
+    # Cold phases: each after an untimed 1 GiB write; then the same single
+    # phases without the write.  The difference to the back-to-back steps
+    # is launch ramp-up and drain, the difference between the two is what
+    # the caches kept between kernels.
     scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    cold_v, cold_c = [], []
+    cold = [[] for _ in range(P)]
+    iso = [[] for _ in range(P)]
     for k in range(args.cold):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        scratch.fill_(float(k))
-        ev[0].record()
-        drive.verify(wl, 0, counter)
-        ev[1].record()
-        scratch.fill_(float(k) + 0.5)
-        ev[2].record()
-        ctx.commit(wl.state_indices, wl.commit_lens,
-                   record_rows=wl.record_rows)
-        ev[3].record()
-        torch.cuda.synchronize()
-        cold_v.append(ev[0].elapsed_time(ev[1]) * 1e3)
-        cold_c.append(ev[2].elapsed_time(ev[3]) * 1e3)
+        for i, (_, _, n, fn) in enumerate(phases):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            scratch.fill_(float(k) + 0.5 * i)
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            cold[i].append(ev[0].elapsed_time(ev[1]) * 1e3 / n)
     del scratch
-    cold_v.sort()
-    cold_c.sort()
-    # The same single launches without the evicting write: the difference
-    # to the back-to-back steps is launch ramp-up and drain, the difference
-    # to the cold launches is what the caches kept between kernels.
-    iso_v, iso_c = [], []
     for k in range(args.cold):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        drive.verify(wl, 0, counter)
-        ev[1].record()
-        torch.cuda.synchronize()
-        ev[2].record()
-        ctx.commit(wl.state_indices, wl.commit_lens,
-                   record_rows=wl.record_rows)
-        ev[3].record()
-        torch.cuda.synchronize()
-        iso_v.append(ev[0].elapsed_time(ev[1]) * 1e3)
-        iso_c.append(ev[2].elapsed_time(ev[3]) * 1e3)
-    iso_v.sort()
-    iso_c.sort()
+        for i, (_, _, n, fn) in enumerate(phases):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            iso[i].append(ev[0].elapsed_time(ev[1]) * 1e3 / n)
+    for xs in cold + iso:
+        xs.sort()
 
-    tokens = nbytes["tokens"]
-    kernels = {
-        "kda_verify_grid_kernel": (nbytes["verify"], v_ms),
-        "kda_commit_grid_kernel": (nbytes["commit"], c_ms),
-    }
-    dom = max(kernels, key=lambda k: kernels[k][1])
-    by, ms = kernels[dom]
+    dom = max(range(P), key=lambda i: mean_ms[i] * phases[i][2])
+    kname, by_step, n_launch, _ = phases[dom]
+    ms = mean_ms[dom]
+    by = by_step / n_launch
     achieved = by / (ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(dom, args.workload)
+    traffic = traffic_from_profiles(kname, args.workload)
+    step_bytes = sum(ph[1] for ph in phases)
     result = {
         "metric": "verified tokens/s (KDA verify+commit, H=32 K=V=128, Q=4)",
         "value": tokens / (ms_step * 1e-3),
@@ -297,7 +373,7 @@ def main() -> int:
         "data": "synthetic (seeded decode batch, bf16 activations, fp32 "
                 "state)",
         "config": {"workload": f"{args.workload}: B={wl.B} H={wl.H} "
-                               f"K=V={wl.D} Q={wl.Q} layers=1 "
+                               f"K=V={wl.D} Q={wl.Q} {note} "
                                f"pool={wl.N} slots "
                                f"conv={'dim-first' if wl.conv_dim_first else 'token-first'}",
                    "batch": wl.B, "heads": wl.H, "head_dim": wl.D,
@@ -305,24 +381,25 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": dom, "bytes_per_launch": by,
+                     "kernel": kname, "bytes_per_launch": by,
                      "us_per_launch": ms * 1e3},
-        "step_hbm": {"bytes": nbytes["verify"] + nbytes["commit"],
-                     "GB/s": (nbytes["verify"] + nbytes["commit"])
-                     / (ms_step * 1e-3) / 1e9,
-                     "frac": (nbytes["verify"] + nbytes["commit"])
-                     / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "verify_us": v_ms * 1e3, "commit_us": c_ms * 1e3,
-                     "verify_GB/s": nbytes["verify"] / (v_ms * 1e-3) / 1e9,
-                     "commit_GB/s": nbytes["commit"] / (c_ms * 1e-3) / 1e9},
+        "step_hbm": dict(
+            {"bytes": step_bytes,
+             "GB/s": step_bytes / (ms_step * 1e-3) / 1e9,
+             "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            **{f"{ph[0]}_us_per_launch": m * 1e3
+               for ph, m in zip(phases, mean_ms)},
+            **{f"{ph[0]}_GB/s": ph[1] / ph[2] / (m * 1e-3) / 1e9
+               for ph, m in zip(phases, mean_ms)}),
         "kernels": {
-            name: {"median_us": quant(xs, 0.5), "p10_us": quant(xs, 0.1),
-                   "p90_us": quant(xs, 0.9),
-                   "single_launch_median_us": quant(si, 0.5) if si else None,
-                   "cold_median_us": quant(cs, 0.5) if cs else None}
-            for name, xs, si, cs in (
-                ("kda_verify_grid_kernel", v_all, iso_v, cold_v),
-                ("kda_commit_grid_kernel", c_all, iso_c, cold_c))},
+            ph[0]: {"median_us": quant(per[i], 0.5),
+                    "p10_us": quant(per[i], 0.1),
+                    "p90_us": quant(per[i], 0.9),
+                    "single_launch_median_us":
+                        quant(iso[i], 0.5) if iso[i] else None,
+                    "cold_median_us": quant(cold[i], 0.5) if cold[i] else None,
+                    "launches_per_step": ph[2]}
+            for i, ph in enumerate(phases)},
     }
     if args.cpu_seconds > 0:
         print("# cpu baseline ...", file=sys.stderr, flush=True)

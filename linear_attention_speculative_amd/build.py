@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -31,6 +32,10 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-kernel resource usage, checked for spills after each compile.
+REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc",
                  shutil.which("hipcc")):
@@ -44,13 +49,31 @@ def _run(cmd, verbose):
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
                          text=True)
-    out = "\n".join(line for line in res.stdout.splitlines()
-                    if "packed-fp32-ops' is not a recognized" not in line)
+    lines = [line for line in res.stdout.splitlines()
+             if "packed-fp32-ops' is not a recognized" not in line]
     if res.returncode != 0:
         raise RuntimeError(f"command failed ({res.returncode}): "
-                           f"{' '.join(cmd)}\n{out}")
+                           f"{' '.join(cmd)}\n" + "\n".join(lines))
+    _check_no_spills(lines)
+    out = "\n".join(line for line in lines if "remark:" not in line and
+                    "Rpass-analysis" not in line)
     if verbose and out.strip():
         print(out)
+
+
+def _check_no_spills(lines):
+    """Every kernel must run without scratch (register spills): the
+    resource-usage remarks of the compiler name each kernel, then its
+    per-lane scratch size."""
+    kernel = None
+    for line in lines:
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            kernel = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            raise RuntimeError(f"kernel {kernel} spills {m.group(1)} bytes "
+                               "per lane to scratch")
 
 
 def build_library(verbose: bool = False) -> str:
@@ -64,7 +87,8 @@ def build_library(verbose: bool = False) -> str:
         path = os.path.join(CSRC, src)
         obj = os.path.join(BUILD_DIR, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        jobs.append([hipcc] + COMMON_FLAGS + lang + ["-c", path, "-o", obj])
+        jobs.append([hipcc] + COMMON_FLAGS + lang + REMARKS +
+                    ["-c", path, "-o", obj])
         objs.append(obj)
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))

@@ -67,15 +67,20 @@ struct VerifyCfg {
   static constexpr int NV = 2 * QMAX + NM + NN;     // reduced scalars
   static constexpr int DS = 2 * QMAX + 4;           // padded row of dots
   // LDS reduction tree: columns are summed in chunks of CH, NB scalars at
-  // a time (the whole set when it fits in 48 KiB).
+  // a time (the whole set when it fits in 20 KiB: at Q = 8 that keeps the
+  // workgroup under 40 KiB of LDS, so four of them fit on a CU).
   static constexpr int CH = D >= 32 ? 32 : D;
   static constexpr int NCH = D / CH;
-  static constexpr int NB = NV * D <= 12288 ? NV : 12288 / D;
+  static constexpr int NB = NV * D <= 5120 ? NV : 5120 / D;
   static constexpr int PART = NB * D > D * DS ? NB * D : D * DS;
   static constexpr int JC = (3 * D + NT - 1) / NT;  // conv channels/thread
   static constexpr int JG = (QMAX * D + NT - 1) / NT;  // gate values/thread
-  // Keep the register budget for 4 waves per SIMD.
-  static constexpr int MIN_WAVES = 4;
+  // Register budget: 4 waves per SIMD up to Q = 4 (LDS allows 4
+  // workgroups per CU), 3 at Q = 8 (the most that fits without spills),
+  // 1 at Q = 16.  The ticket loop carries more live state: 2 at Q = 8.
+  // No instantiation may spill (the build checks it).
+  static constexpr int MIN_WAVES = QMAX >= 16 ? 1 : QMAX >= 8 ? 3 : 4;
+  static constexpr int TICKET_MIN_WAVES = QMAX >= 16 ? 1 : QMAX >= 8 ? 2 : 4;
   static_assert(RPP * PASSES == D, "tile rows");
   static_assert(CHUNKS * 4 * L == D, "tile columns");
   static_assert(NVAL <= L, "one row sum per lane");
@@ -86,7 +91,11 @@ struct alignas(16) VerifySmem {
   using C = VerifyCfg<D, QMAX>;
   float y[3][QMAX][D];           // conv outputs q | k | v, positions < q
   float dec[QMAX][D];            // decays d_t
-  float vec[2 * QMAX][D];        // Gam_t k_hat_t, then Gam_t q_hat_t
+  // Gam_t k_hat_t, then Gam_t q_hat_t: written in phase 2 over y's q and k
+  // rows, which phase 1 has read into registers (only v is read later)
+  __device__ float (*vec())[D] {
+    return reinterpret_cast<float (*)[D]>(&y[0][0][0]);
+  }
   // column partial sums [NB][D] (phase 1), then per row:
   // S.(Gam k_hat_t), S.(Gam q_hat_t) [D][DS] (phases 3-4)
   float part[C::PART];
@@ -464,8 +473,8 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
       gam *= dd[t];
       const float rk = rsqrtf(total(t) + kNormEps);
       const float rq = rsqrtf(total(QMAX + t) + kNormEps) * inv_sqrt_d;
-      sm.vec[t][tid] = gam * kk[t] * rk;
-      sm.vec[QMAX + t][tid] = gam * qq[t] * rq;
+      sm.vec()[t][tid] = gam * kk[t] * rk;
+      sm.vec()[QMAX + t][tid] = gam * qq[t] * rq;
     }
   }
   for (int j = tid; j < QMAX * QMAX; j += C::NT) {
@@ -501,8 +510,8 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
 #pragma unroll
       for (int c = 0; c < C::CHUNKS; ++c) {
         const int cc = c * 4 * C::L + 4 * lg;
-        ka[c] = *reinterpret_cast<const f4*>(&sm.vec[t][cc]);
-        qa[c] = *reinterpret_cast<const f4*>(&sm.vec[QMAX + t][cc]);
+        ka[c] = *reinterpret_cast<const f4*>(&sm.vec()[t][cc]);
+        qa[c] = *reinterpret_cast<const f4*>(&sm.vec()[QMAX + t][cc]);
       }
       float acc[C::NVAL];
 #pragma unroll
@@ -817,7 +826,7 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
 
 template <int D, int QMAX, bool ACT_BF16>
 __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
-                                  (VerifyCfg<D, QMAX>::MIN_WAVES))
+                                  (VerifyCfg<D, QMAX>::TICKET_MIN_WAVES))
     kda_verify_kernel(VerifyParams p) {
   using C = VerifyCfg<D, QMAX>;
   __shared__ VerifySmem<D, QMAX> sm;
