@@ -308,7 +308,9 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
   const int64_t s_tok = a->conv_dim_first ? cs.stride[2] : cs.stride[1];
   if (C3 * s_chan + Lc * s_tok > i32max || C3 * cw.stride[0] > i32max ||
       Q * (a->mixed_qkv.stride[0] + a->raw_gate.stride[0] +
-           a->raw_beta.stride[0] + a->out.stride[0]) > i32max)
+           a->raw_beta.stride[0] + a->out.stride[0]) > i32max ||
+      Q * (a->correction.stride[2] + a->key_gate.stride[2]) + 2 * D >
+          i32max)
     return fail(KDA_E_LAYOUT, "per-request offsets exceed 2^31 elements");
 
   kda::VerifyParams& p = plan->p;

@@ -540,9 +540,12 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
   // ---- phase 4: per-row triangular solve, outputs and corrections -------------
   if (tid < D) {
     const int v = tid;
+    // wave-uniform bases, 32-bit per-lane offsets
     float* __restrict__ corr = p.correction + int64_t(it.r) * p.s_c_row +
-                               int64_t(h) * p.s_c_head + v;
-    const int64_t ob = int64_t(it.bos) * p.s_out + h * D + v;
+                               int64_t(h) * p.s_c_head;
+    const int64_t ob = int64_t(it.bos) * p.s_out + h * D;
+    float* __restrict__ out32 = static_cast<float*>(p.out) + ob;
+    uint16_t* __restrict__ out16 = static_cast<uint16_t*>(p.out) + ob;
     const int s_cp = p.s_c_pos, s_out = p.s_out;
     const float* drow = &sm.part[v * C::DS];
     float cc[QMAX];
@@ -557,10 +560,10 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
 #pragma unroll
         for (int s = 0; s <= t; ++s) o = fmaf(sm.Nc[t][s], cc[s], o);
         if (p.flags & kOutBf16)
-          static_cast<uint16_t*>(p.out)[ob + t * s_out] = f32_to_bf16(o);
+          at(out16, uint32_t(t * s_out + v)) = f32_to_bf16(o);
         else
-          static_cast<float*>(p.out)[ob + t * s_out] = o;
-        if (rec_ok) corr[t * s_cp] = cc[t];
+          at(out32, uint32_t(t * s_out + v)) = o;
+        if (rec_ok) at(corr, uint32_t(t * s_cp + v)) = cc[t];
       }
     }
   }
