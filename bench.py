@@ -20,7 +20,9 @@ the timed steps, the median of single synchronized launches, and the
 median of single launches that each follow an untimed 1 GiB write (which
 evicts the caches), so that any help from the last-level cache between
 kernels shows up as a difference; `cpu_baseline`
-times the fp64 CPU oracle on a bounded sample of the same workload.
+times the fp64 CPU oracle on a bounded sample of the same workload;
+`deferred_form` (headline only) times the same batch in the deferred form
+(see `--workload fused`) as context for the headline figure.
 
 Other workloads (`--workload`), each one JSON line of the same form:
   large     24 layers: 24 verifies, then one commit launch over all layers
@@ -30,7 +32,11 @@ Other workloads (`--workload`), each one JSON line of the same form:
             into the checkpoint and then verifies;
   align     the headline batch under prefix caching (16-token state
             blocks): verify of the running block, then the commit plan,
-            conv compaction and align-mode commit.
+            conv compaction and align-mode commit;
+  fused     the headline batch in the deferred form: each step is one
+            launch that folds the previous step's accepted positions into
+            the checkpoints and then verifies (the same verify and commit
+            work per step, one state pass fewer).
 The default run (headline) is the one the throughput figure is quoted on.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
@@ -130,7 +136,7 @@ def build_phases(name, wl, drive, torch):
     import numpy as np
     counter = torch.zeros(1, dtype=torch.int32, device="cuda")
     L = len(wl.layers)
-    if name == "deferred":
+    if name in ("deferred", "fused"):
         nb = algorithmic_bytes(wl, pending=wl.commit_lens.cpu().numpy())
 
         def fused():
@@ -138,7 +144,8 @@ def build_phases(name, wl, drive, torch):
                 drive.verify(wl, layer, counter, pending_lens=wl.commit_lens)
         return ([("kda_verify_grid_kernel", (nb["verify"] + nb["flush"]) * L,
                   L, fused)], nb["tokens"] * L,
-                f"layers={L} fused flush+verify, pending 0..{wl.Q}")
+                f"layers={L} fused flush+verify, pending "
+                f"{int(wl.commit_lens.min())}..{int(wl.commit_lens.max())}")
     ctx = drive.commit_context(wl, conv=name == "align")
     if name == "align":
         bs = 16
@@ -283,7 +290,8 @@ def main() -> int:
     from workloads import make_workload
     from workloads import drive
 
-    cfg_name = "headline" if args.workload == "align" else args.workload
+    cfg_name = "headline" if args.workload in ("align", "fused") \
+        else args.workload
     wl = make_workload(cfg_name, "cuda", out_dtype="act")
     phases, tokens, note = build_phases(args.workload, wl, drive, torch)
     P = len(phases)
@@ -401,6 +409,28 @@ def main() -> int:
                     "launches_per_step": ph[2]}
             for i, ph in enumerate(phases)},
     }
+    if args.workload == "headline":
+        # Context, not the headline figure: the same batch in the deferred
+        # form of the state page (commit of the previous step folded into
+        # this step's verify launch).
+        fphases, ftokens, fnote = build_phases("fused", wl, drive, torch)
+        ffn = fphases[0][3]
+        for _ in range(args.warmup):
+            ffn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            ffn()
+        torch.cuda.synchronize()
+        fms = (time.perf_counter() - t0) * 1e3 / args.steps
+        fby = fphases[0][1]
+        result["deferred_form"] = {
+            "value": ftokens / (fms * 1e-3), "unit": "verified tokens/s",
+            "ms_per_step": fms, "step": fnote,
+            "GB/s": fby / (fms * 1e-3) / 1e9,
+            "frac": fby / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        print(f"# deferred form: {fms:.4f} ms/step", file=sys.stderr,
+              flush=True)
     if args.cpu_seconds > 0:
         print("# cpu baseline ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
