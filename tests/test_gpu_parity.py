@@ -525,3 +525,38 @@ def test_unfused_verify_headline_sampled():
     reqs = list(range(0, wl.B, 17)) + [wl.B - 1]
     sample, ref, errs = _qkv_case(wl, reqs=reqs)
     print("qkv headline", errs)
+
+
+def test_deferred_flush_with_unfused_verify():
+    # The fused flush in front of the unfused verify: commit of the pending
+    # positions, then the verify of convolved q | k | v from the committed
+    # state; the conv state is not touched.
+    for D, Q, act in ((128, 4, "bf16"), (64, 8, "f32")):
+        wl = make_workload("ragged", DEV, B=16, H=3, D=D, Q=Q, N=32, act=act,
+                           weight=act, null_frac=0.15)
+        rng = np.random.default_rng(D + 7 * Q)
+        qlen = (wl.query_start_loc[1:] - wl.query_start_loc[:-1]).cpu().numpy()
+        pend = np.minimum(rng.integers(0, Q + 1, size=wl.B), qlen)
+        wl.commit_lens.copy_(torch.tensor(pend, dtype=torch.int32))
+        L = wl.layers[0]
+        s0 = snapshot(wl, 0)
+        drive.verify_qkv(wl, 0, _counter())
+        torch.cuda.synchronize()
+        r0 = run_oracle_verify_qkv(s0)
+        (new, written), = oracle.commit(
+            layers=[commit_layer_inputs(s0, r0, L)],
+            state_indices=s0.new_slot, commit_lens=pend[s0.reqs],
+            spec_query_len=wl.Q, record_rows=s0.new_row)
+        s1 = snapshot(wl, 0)
+        inp = {k: v for k, v in s0.inputs.items()
+               if k not in ("conv_state", "conv_weight", "num_accepted_tokens")}
+        inp.update(state=new, correction=r0["correction"],
+                   key_gate=r0["key_gate"])
+        ref1 = oracle.verify_qkv(**inp)
+        conv_before = L.conv_state.clone()
+        drive.verify_qkv(wl, 0, _counter(), pending_lens=wl.commit_lens)
+        torch.cuda.synchronize()
+        assert torch.equal(L.conv_state, conv_before)
+        cerr = check_commit(wl, 0, s0, new, written)
+        errs = check_verify(wl, 0, s1, ref1)
+        print("flush qkv", D, Q, act, cerr, errs)
