@@ -319,6 +319,71 @@ def test_verify_graph_replay_matches_eager():
         assert torch.equal(L.page, eager_page)
 
 
+def _graph_matches_eager(run, reset, outputs):
+    """Capture run() in a HIP graph; replay it three times with eager
+    resets in between and compare every replay with an eager run, bit for
+    bit."""
+    reset()
+    torch.cuda.synchronize()
+    run()
+    torch.cuda.synchronize()
+    eager = [bits(t) for t in outputs()]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outputs(), eager):
+            assert np.array_equal(bits(a), b)
+
+
+def test_commit_flush_and_align_graph_replay_matches_eager():
+    wl = make_workload("ragged", DEV, B=16, H=4, D=128, Q=4, N=48,
+                       null_frac=0.1)
+    L = wl.layers[0]
+    drive.verify(wl, 0, _counter())            # records to commit
+    torch.cuda.synchronize()
+    page0 = L.page.clone()
+
+    def reset():
+        L.page.copy_(page0)
+        L.out.fill_(float("nan"))
+
+    ctx = drive.commit_context(wl, conv=True)
+    # the multi-layer commit
+    _graph_matches_eager(
+        lambda: ctx.commit(wl.state_indices, wl.commit_lens), reset,
+        lambda: [L.page])
+    # the fused deferred flush + verify
+    _graph_matches_eager(
+        lambda: drive.verify(wl, 0, _counter(), pending_lens=wl.commit_lens),
+        reset, lambda: [L.page, L.out])
+    # plan, compaction and align-mode commit in one call
+    rng = np.random.default_rng(3)
+    slots = wl.state_indices.cpu().numpy()
+    free = [x for x in range(1, wl.N) if x not in set(slots.tolist())]
+    table = np.zeros((wl.B, 2), dtype=np.int32)
+    table[:, 0] = slots
+    table[:, 1] = free[:wl.B]
+    table_t = torch.as_tensor(table, device=DEV)
+    computed = torch.as_tensor(rng.integers(0, 6, size=wl.B),
+                               dtype=torch.int32, device=DEV)
+    _graph_matches_eager(
+        lambda: ctx.commit_step(wl.commit_lens, wl.state_indices,
+                                wl.query_start_loc, block_table=table_t,
+                                num_computed_tokens=computed,
+                                mamba_block_size=6),
+        reset, lambda: [L.page])
+
+
 # ---- full-size workloads on sampled requests ----------------------------------------
 
 def test_headline_workload_sampled():
