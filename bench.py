@@ -23,7 +23,9 @@ median of single launches that each follow an untimed 1 GiB write (which
 evicts the caches), so that any help from the last-level cache between
 kernels shows up as a difference; `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload;
-`deferred_form` (headline only) times the same batch in the deferred form
+`step_hbm.frac_of_copy` relates the step's bandwidth to a plain 1 GiB
+device copy timed in the same run; `deferred_form` (headline only) times
+the same batch in the deferred form
 (see `--workload fused`) as context for the headline figure.
 
 Other workloads (`--workload`), each one JSON line of the same form:
@@ -395,6 +397,23 @@ def main() -> int:
     for xs in cold + iso:
         xs.sort()
 
+    # A plain 1 GiB device copy on the same GPU, for the fraction of what
+    # this HBM sustains for streaming read + write traffic.
+    csrc = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    cdst = torch.empty_like(csrc)
+    for _ in range(2):
+        cdst.copy_(csrc)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    cev[0].record()
+    for _ in range(5):
+        cdst.copy_(csrc)
+    cev[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * csrc.numel() * 4 * 5 / (cev[0].elapsed_time(cev[1]) *
+                                           1e-3) / 1e9
+    del csrc, cdst
+
     dom = max(range(P), key=lambda i: mean_ms[i] * phases[i][2])
     kname, by_step, n_launch, _ = phases[dom]
     ms = mean_ms[dom]
@@ -432,7 +451,9 @@ def main() -> int:
         "step_hbm": dict(
             {"bytes": step_bytes,
              "GB/s": step_bytes / (ms_step * 1e-3) / 1e9,
-             "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+             "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+             "copy_GB/s": copy_gbs,
+             "frac_of_copy": step_bytes / (ms_step * 1e-3) / 1e9 / copy_gbs},
             **{f"{ph[0]}_us_per_launch": m * 1e3
                for ph, m in zip(phases, mean_ms)},
             **{f"{ph[0]}_GB/s": ph[1] / ph[2] / (m * 1e-3) / 1e9
