@@ -895,10 +895,9 @@ __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
     atomicExch(p.counter, 0);
 }
 
-// One workgroup per (head, request) item: blockIdx.x = head, blockIdx.y =
-// request, so the hardware dispatcher hands out items in request-major
-// order and refills each compute unit as workgroups retire (which also
-// balances ragged windows).  No loop-carried state, no ticket counter.
+// One workgroup per (head, request) item on a (head, request) grid; the
+// hardware dispatcher refills each compute unit as workgroups retire (which
+// also balances ragged windows).  No loop-carried state, no ticket counter.
 // FLUSH: the deferred flush of pending record positions comes first.
 template <int D, int QMAX, bool ACT_BF16, bool FLUSH>
 __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
@@ -907,7 +906,15 @@ __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
   using C = VerifyCfg<D, QMAX>;
   __shared__ VerifySmem<D, QMAX> sm;
   __shared__ FlushSmem<D, QMAX, FLUSH> fs;
-  const Item it = load_item(p, int(blockIdx.y), int(blockIdx.x));
+  // XCD-aware order: the dispatcher hands consecutive workgroups to the 8
+  // XCDs in turn, so workgroup i takes item (i mod 8) * n/8 + i/8 and each
+  // XCD works through one contiguous eighth of the (request, head) items
+  // (4% faster for the fused flush at 1024 requests, neutral otherwise).
+  const int n = p.B * p.H;
+  const int lin = int(blockIdx.x) + p.H * int(blockIdx.y);
+  const int item = (n & 7) == 0 ? (lin & 7) * (n >> 3) + (lin >> 3) : lin;
+  const int ib = item / p.H;
+  const Item it = load_item(p, uniform(ib), uniform(item - ib * p.H));
   auto advance = [] {};
   if (it.live) {
     if (it.q == QMAX)
