@@ -9,6 +9,7 @@ import torch
 
 import linear_attention_speculative_amd as kda
 import oracle
+from linear_attention_speculative_amd.debug import check_slot_aliasing
 from tests.gpu_check import TOL, bits, f64, rel_err
 from workloads import drive, make_workload
 from workloads.gen import block_tables, step_activations
@@ -36,7 +37,10 @@ def _destinations(rng, sources, N):
         final.append(int(s) if rng.random() < 0.4 else free.pop())
         r = rng.random()
         bnd.append(0 if r < 0.3 else (int(s) if r < 0.5 else free.pop()))
-    return np.array(final), np.array(bnd)
+    final, bnd = np.array(final), np.array(bnd)
+    check_slot_aliasing(sources, num_slots=N, final_state_indices=final,
+                        boundary_state_indices=bnd)
+    return final, bnd
 
 
 # ---- the plan ------------------------------------------------------------------
