@@ -97,7 +97,8 @@ typedef enum {
   KDA_SCHEDULE_DEFAULT = 0,    /* the library's choice (the fastest measured
                                   for the shape) */
   KDA_SCHEDULE_PER_ITEM = 1,   /* one workgroup per item, handed out by the
-                                  hardware dispatcher in request-major order */
+                                  hardware dispatcher (each XCD takes one
+                                  contiguous eighth of the items) */
   KDA_SCHEDULE_TICKETS = 2     /* persistent workgroups drawing tickets of
                                   items_per_ticket items from work_counter
                                   (the kernels page's design) */
@@ -149,7 +150,9 @@ typedef struct {
                               schedules. */
   int32_t batch;
   int32_t spec_query_len;  /* Q */
-  int32_t null_block_id;   /* slots <= this are null (0 in vLLM) */
+  int32_t null_block_id;   /* slots <= this are null (the ops page imports
+                              the value without printing it; the tests
+                              use 0) */
   int32_t conv_dim_first;  /* 1: conv_state is [N, 3HD, Lc]; 0: [N, Lc, 3HD] */
   int32_t use_lower_bound; /* 1: g = lower_bound*sigmoid(A x); 0: softplus */
   float lower_bound;
