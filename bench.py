@@ -36,7 +36,7 @@ Other workloads (`--workload`), each one JSON line of the same form:
             into the checkpoint and then verifies;
   align     the headline batch under prefix caching (16-token state
             blocks): verify of the running block, then the commit plan,
-            conv compaction and align-mode commit;
+            conv compaction and align-mode commit in one fused launch;
   fused     the headline batch in the deferred form: each step is one
             launch that folds the previous step's accepted positions into
             the checkpoints and then verifies (the same verify and commit
@@ -60,6 +60,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+ALIGN_BLOCK_SIZE = 16          # tokens per state block, align workload
 KERNEL_SOURCES = {
     "kda_verify_grid_kernel": "kda_verify.hip",
     "kda_commit_grid_kernel": "kda_commit.hip",
@@ -152,14 +153,10 @@ def build_phases(name, wl, drive, torch):
                 f"{int(wl.commit_lens.min())}..{int(wl.commit_lens.max())}")
     ctx = drive.commit_context(wl, conv=name == "align")
     if name == "align":
-        bs = 16
-        rng = np.random.default_rng(5)
-        slots = wl.state_indices.cpu().numpy()
-        free = [s for s in range(1, wl.N) if s not in set(slots.tolist())]
-        table = np.zeros((wl.B, 2), dtype=np.int32)
-        table[:, 0] = slots
-        table[:len(free), 1] = free[:wl.B]
-        computed = rng.integers(0, bs, size=wl.B).astype(np.int32)
+        from workloads.gen import running_block_tables
+        bs = ALIGN_BLOCK_SIZE
+        table, computed = running_block_tables(
+            wl.state_indices.cpu().numpy(), wl.N, bs, seed=5)
         lens = wl.commit_lens.cpu().numpy()
         boundary = np.where(computed + lens >= bs, bs - computed, 0)
         nb = algorithmic_bytes(wl, boundary=boundary)
@@ -178,11 +175,12 @@ def build_phases(name, wl, drive, torch):
                             wl.query_start_loc, block_table=table_t,
                             num_computed_tokens=computed_t,
                             mamba_block_size=bs)
+        # one launch: the commit kernel plans and compacts inline
         return ([("kda_verify_grid_kernel", nb["verify"], 1, verify),
-                 ("commit_step(plan+compaction+commit)",
-                  nb["commit"] + nb["compact"], 1, commit)], nb["tokens"],
+                 ("kda_commit_grid_kernel", nb["commit"] + nb["compact"], 1,
+                  commit)], nb["tokens"],
                 f"layers=1 align bs={bs}, {int((boundary > 0).sum())} "
-                "boundaries per step")
+                "boundaries per step, fused commit step")
     nb = algorithmic_bytes(wl)
 
     def verify_all():

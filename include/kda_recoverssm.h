@@ -29,6 +29,9 @@
  *       state commit: the per-request plan (commit lengths, final and
  *       boundary slots) and the conv-state compaction.
  *
+ *   kda_recoverssm_commit_step -- those three (plan, compaction, commit)
+ *       with the same results, in one launch.
+ *
  * plus host-only argument checks mirroring the pages' validation
  * (kernels page `_check_layouts`, `can_use_cute_recoverssm`; ops page
  * `kda_recoverssm_verify`, `KDARecoverSSMCommitContext.create/commit`).
@@ -66,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 /* Status codes. */
 typedef enum {
@@ -349,6 +352,30 @@ int kda_commit_plan(const kda_plan_args* args, void* stream);
    `stream` (one thread per layer, request and channel). */
 int kda_check_compact_conv(const kda_compact_args* args);
 int kda_compact_conv_state(const kda_compact_args* args, void* stream);
+
+/* The whole of the ops page's `KDARecoverSSMCommitContext.commit` in one
+   launch: the results of kda_commit_plan(plan), then, when `compact` is not
+   NULL, kda_compact_conv_state(compact), then kda_recoverssm_commit(commit),
+   bit for bit.  Every (layer, request, head) workgroup of the commit plans
+   its request itself (the layer-0, head-0 one writes the plan's four
+   outputs) and copies that head's conv histories (its q, k and v channels)
+   before its state fold.
+   The three blocks must describe the calls the separate path would make:
+   one batch, window and null id; the commit's state_indices, commit_lens
+   and final_state_indices (and, iff the plan has a block table, its
+   boundary pair) are the plan's state_indices and output pointers, and so
+   are the compaction's; the compaction covers the commit's layers and slot
+   count with conv_dim = 3 * num_heads * head_dim.  Otherwise KDA_E_ARG.
+   The plan's output arrays are written, never read, by the launch.  The
+   slot rules of the separate calls hold: no request's final or boundary
+   slot is another request's source or destination. */
+int kda_check_commit_step(const kda_commit_args* commit,
+                          const kda_plan_args* plan,
+                          const kda_compact_args* compact);
+int kda_recoverssm_commit_step(const kda_commit_args* commit,
+                               const kda_plan_args* plan,
+                               const kda_compact_args* compact,
+                               void* stream);
 
 /* Launch a one-workgroup kernel that sets counter[0..n) to 0 on `stream`
    (for a counter left non-zero by an aborted launch).  Uses no memset

@@ -32,7 +32,9 @@ EXPORTED = (
     "kda_check_verify", "kda_conv_update_verify", "kda_check_verify_qkv",
     "kda_recoverssm_verify_qkv", "kda_check_commit",
     "kda_recoverssm_commit", "kda_check_commit_plan", "kda_commit_plan",
-    "kda_check_compact_conv", "kda_compact_conv_state", "kda_reset_counter",
+    "kda_check_compact_conv", "kda_compact_conv_state",
+    "kda_check_commit_step", "kda_recoverssm_commit_step",
+    "kda_reset_counter",
 )
 
 
@@ -156,6 +158,15 @@ def load() -> ctypes.CDLL:
     lib.kda_check_compact_conv.argtypes = [POINTER(KdaCompactArgs)]
     lib.kda_compact_conv_state.restype = c_int
     lib.kda_compact_conv_state.argtypes = [POINTER(KdaCompactArgs), c_void_p]
+    lib.kda_check_commit_step.restype = c_int
+    lib.kda_check_commit_step.argtypes = [POINTER(KdaCommitArgs),
+                                          POINTER(KdaPlanArgs),
+                                          POINTER(KdaCompactArgs)]
+    lib.kda_recoverssm_commit_step.restype = c_int
+    lib.kda_recoverssm_commit_step.argtypes = [POINTER(KdaCommitArgs),
+                                               POINTER(KdaPlanArgs),
+                                               POINTER(KdaCompactArgs),
+                                               c_void_p]
     lib.kda_reset_counter.restype = c_int
     lib.kda_reset_counter.argtypes = [c_void_p, c_int32, c_void_p]
     _LIB = lib

@@ -616,6 +616,66 @@ int plan_compact(const kda_compact_args* a, kda::CompactParams* p,
   return KDA_OK;
 }
 
+// Fused commit step: the three argument blocks must describe one batch
+// exactly as they would for the three separate calls (the commit and the
+// compaction read the plan's output arrays).
+bool reads_plan(const int32_t* si, const int32_t* lens, const int32_t* fin,
+                const int32_t* bnd, const int32_t* blen,
+                const kda_plan_args* pl) {
+  const bool align = pl->block_table != nullptr;
+  return si == pl->state_indices && lens == pl->commit_lens &&
+         fin == pl->final_state_indices &&
+         (align ? (bnd == pl->boundary_state_indices &&
+                   blen == pl->boundary_recovery_lens)
+                : (bnd == nullptr && blen == nullptr));
+}
+
+int plan_step(const kda_commit_args* c, const kda_plan_args* pl,
+              const kda_compact_args* cp, CommitPlan* plan) {
+  if (c == nullptr || pl == nullptr)
+    return fail(KDA_E_ARG, "the commit step needs commit and plan arguments");
+  KDA_TRY(plan_commit(c, plan));
+  kda::PlanParams pp;
+  KDA_TRY(plan_plan(pl, &pp));
+  if (pl->batch != c->batch || pl->spec_query_len != c->spec_query_len ||
+      pl->null_block_id != c->null_block_id)
+    return fail(KDA_E_ARG, "commit step: the plan and the commit describe "
+                           "different batches");
+  if (c->batch > 0 &&
+      !reads_plan(c->state_indices, c->commit_lens, c->final_state_indices,
+                  c->boundary_state_indices, c->boundary_recovery_lens, pl))
+    return fail(KDA_E_ARG,
+                "commit step: the commit must take the plan's state_indices "
+                "and its output arrays (boundary pair only in align mode)");
+  plan->p.step = 1;
+  plan->p.plan = pp;
+  if (cp != nullptr) {
+    kda::CompactParams q;
+    int e = 0;
+    KDA_TRY(plan_compact(cp, &q, &e));
+    if (cp->batch != c->batch || cp->num_layers != c->num_layers ||
+        cp->spec_query_len != c->spec_query_len ||
+        cp->null_block_id != c->null_block_id ||
+        cp->num_slots != c->num_slots ||
+        cp->conv_dim != 3 * int64_t(c->num_heads) * c->head_dim)
+      return fail(KDA_E_ARG,
+                  "commit step: the compaction and the commit describe "
+                  "different batches, layers or pools (conv_dim must be "
+                  "3 * heads * head_dim)");
+    if (c->batch > 0 &&
+        !reads_plan(cp->state_indices, cp->commit_lens,
+                    cp->final_state_indices, cp->boundary_state_indices,
+                    cp->boundary_recovery_lens, pl))
+      return fail(KDA_E_ARG,
+                  "commit step: the compaction must take the plan's "
+                  "state_indices and its output arrays (boundary pair only "
+                  "in align mode)");
+    plan->p.conv_tables = cp->conv_tables;
+    plan->p.conv_elem = e;
+  }
+  return KDA_OK;
+}
+
 int device_status(int hip_rc, const char* what) {
   if (hip_rc == 0) return KDA_OK;
   return fail(KDA_E_DEVICE, "%s: HIP error %d (%s)", what, hip_rc,
@@ -728,6 +788,27 @@ int kda_compact_conv_state(const kda_compact_args* args, void* stream) {
   return device_status(
       kda::launch_compact(p, e, static_cast<hipStream_t>(stream)),
       "kda_compact_conv_state launch");
+}
+
+int kda_check_commit_step(const kda_commit_args* commit,
+                          const kda_plan_args* plan,
+                          const kda_compact_args* compact) {
+  g_err.clear();
+  CommitPlan cp;
+  return plan_step(commit, plan, compact, &cp);
+}
+
+int kda_recoverssm_commit_step(const kda_commit_args* commit,
+                               const kda_plan_args* plan,
+                               const kda_compact_args* compact,
+                               void* stream) {
+  g_err.clear();
+  CommitPlan cp;
+  KDA_TRY(plan_step(commit, plan, compact, &cp));
+  if (cp.noop) return KDA_OK;
+  return device_status(
+      kda::launch_commit(cp.p, cp.D, static_cast<hipStream_t>(stream)),
+      "kda_recoverssm_commit_step launch");
 }
 
 int kda_reset_counter(int32_t* counter, int32_t n, void* stream) {

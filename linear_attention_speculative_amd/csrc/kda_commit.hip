@@ -28,8 +28,9 @@
 // one slot and their records together in that XCD's L2 (8% faster on a
 // 24-layer commit, 1.5% on one layer).  With grid > 0, a persistent grid of
 // that many workgroups walks the items with a stride.
-#include "kda_device.hpp"
-#include "kda_internal.hpp"
+#include <type_traits>
+
+#include "kda_step.hpp"
 
 namespace kda {
 namespace {
@@ -70,31 +71,173 @@ struct alignas(16) CommitSmem {
   BoundarySmem<D, QMAX, ALIGN> bd;
 };
 
+// Conv histories of one head for the fused step: channels part*H*D + h*D + d
+// (part < 3: the q, k and v blocks), W - 1 entries each for the final slot
+// and the boundary slot, held as 32-bit words between the loads and the
+// stores.
+template <int D, int NT>
+struct HeadHistories {
+  static constexpr int CH = (3 * D + NT - 1) / NT;  // channels per thread
+  uint32_t fin[CH][kConvWidth - 1];
+  uint32_t bnd[CH][kConvWidth - 1];
+};
+
+template <int D, int NT, class T>
+__device__ __forceinline__ void load_head_histories(
+    HeadHistories<D, NT>& hh, const T* src, int64_t s_ch, int64_t s_tok,
+    int64_t head_ch, int64_t part_ch, int n, int m, bool bnd) {
+#pragma unroll
+  for (int c = 0; c < HeadHistories<D, NT>::CH; ++c) {
+    const int j = int(threadIdx.x) + c * NT;
+    if (j < 3 * D) {
+      const int part = j / D;
+      const T* row = src + (head_ch + part * part_ch + (j - part * D)) * s_ch;
+      const ConvHistory<T> a = load_history(row, s_tok, n);
+#pragma unroll
+      for (int i = 0; i < kConvWidth - 1; ++i) hh.fin[c][i] = a.v[i];
+      if (bnd) {
+        const ConvHistory<T> e = load_history(row, s_tok, m);
+#pragma unroll
+        for (int i = 0; i < kConvWidth - 1; ++i) hh.bnd[c][i] = e.v[i];
+      }
+    }
+  }
+}
+
+template <int D, int NT, class T>
+__device__ __forceinline__ void store_head_histories(
+    const HeadHistories<D, NT>& hh, T* fdst, T* bdst, int64_t s_ch,
+    int64_t s_tok, int64_t head_ch, int64_t part_ch) {
+#pragma unroll
+  for (int c = 0; c < HeadHistories<D, NT>::CH; ++c) {
+    const int j = int(threadIdx.x) + c * NT;
+    if (j < 3 * D) {
+      const int part = j / D;
+      const int64_t off = (head_ch + part * part_ch + (j - part * D)) * s_ch;
+      if (bdst) {                                       // boundary first
+        ConvHistory<T> e;
+#pragma unroll
+        for (int i = 0; i < kConvWidth - 1; ++i) e.v[i] = T(hh.bnd[c][i]);
+        store_history(bdst + off, s_tok, e);
+      }
+      ConvHistory<T> a;
+#pragma unroll
+      for (int i = 0; i < kConvWidth - 1; ++i) a.v[i] = T(hh.fin[c][i]);
+      store_history(fdst + off, s_tok, a);
+    }
+  }
+}
+
+// The fused step's compaction for one (layer, request, head): `load` issues
+// the reads, `store` the writes (after every read of the item).
+template <int D, int NT>
+struct HeadCompaction {
+  HeadHistories<D, NT> hh;
+  bool on = false, bnd = false;
+  int64_t base = 0;
+  int64_t s_slot = 0, s_ch = 0, s_tok = 0, head_ch = 0, part_ch = 0;
+  int slot = 0, f = 0, bslot = 0;
+
+  __device__ __forceinline__ void load(const CommitParams& p, int l, int h,
+                                       int slot_, int n, int f_, int bslot_,
+                                       int m) {
+    on = p.conv_tables != nullptr;
+    if (!on) return;
+    const int64_t L = p.L;
+    base = p.conv_tables[l];
+    s_slot = p.conv_tables[L + l];
+    s_ch = p.conv_tables[2 * L + l];
+    s_tok = p.conv_tables[3 * L + l];
+    head_ch = int64_t(h) * D;
+    part_ch = int64_t(p.H) * D;
+    slot = slot_;
+    f = f_;
+    bslot = bslot_;
+    bnd = bslot_ >= 0 && m >= 1;
+    if (p.conv_elem == 2)
+      load_head_histories<D, NT>(
+          hh, global_addr<const uint16_t>(base) + slot * s_slot, s_ch,
+          s_tok, head_ch, part_ch, n, m, bnd);
+    else
+      load_head_histories<D, NT>(
+          hh, global_addr<const uint32_t>(base) + slot * s_slot, s_ch,
+          s_tok, head_ch, part_ch, n, m, bnd);
+  }
+
+  __device__ __forceinline__ void store(const CommitParams& p) {
+    if (!on) return;
+    if (p.conv_elem == 2) {
+      uint16_t* b16 = global_addr<uint16_t>(base);
+      store_head_histories<D, NT>(hh, b16 + f * s_slot,
+                                  bnd ? b16 + bslot * s_slot : nullptr, s_ch,
+                                  s_tok, head_ch, part_ch);
+    } else {
+      uint32_t* b32 = global_addr<uint32_t>(base);
+      store_head_histories<D, NT>(hh, b32 + f * s_slot,
+                                  bnd ? b32 + bslot * s_slot : nullptr, s_ch,
+                                  s_tok, head_ch, part_ch);
+    }
+  }
+};
+
+template <int D, int NT>
+struct NoCompaction {
+  __device__ __forceinline__ void load(const CommitParams&, int, int, int,
+                                       int, int, int, int) {}
+  __device__ __forceinline__ void store(const CommitParams&) {}
+};
+
 // Commit of one (layer, request, head).  Returns whether it used LDS (a
-// skipped item returns before touching it).
-template <int D, int QMAX, bool ALIGN>
+// skipped item returns before touching it).  STEP: the fused commit step
+// (plan inline, and the conv compaction of this head).
+template <int D, int QMAX, bool ALIGN, bool STEP>
 __device__ __forceinline__ bool commit_item(const CommitParams& p,
                                             CommitSmem<D, QMAX, ALIGN>& sm,
                                             int l, int b, int h) {
   using C = CommitCfg<D, QMAX>;
   const int tid = threadIdx.x;
   const int slot = p.slots[b];
-  if (slot <= p.null_id || slot < 0 || slot >= p.N) return false;
-  const int n = min(max(p.commit_lens[b], 0), p.Q);
-  if (n == 0) return false;
-  const int f = p.final_slots ? p.final_slots[b] : slot;
-  if (f <= p.null_id || f < 0 || f >= p.N) return false;
-  const int r = p.record_rows ? p.record_rows[b] : slot;
-  if (r < 0 || r >= p.R) return false;
+  int n, f;
   // boundary slot (align mode): -1 when there is none to store
   int bslot = -1, m = 0;
-  if constexpr (ALIGN) {
-    bslot = p.bnd_slots[b];
-    m = min(max(p.bnd_lens[b], 0), n);
-    if (bslot <= p.null_id || bslot < 0 || bslot >= p.N) bslot = -1;
+  if constexpr (STEP) {
+    const RequestPlan pl = plan_request(p.plan, b);
+    if (l == 0 && h == 0 && tid == 0) store_plan(p.plan, b, pl);
+    if (slot <= p.null_id || slot < 0 || slot >= p.N) return false;
+    n = pl.n;
+    if (n == 0) return false;
+    f = pl.final_slot;
+    if (f <= p.null_id || f < 0 || f >= p.N) return false;
+    if constexpr (ALIGN) {
+      bslot = pl.bnd;
+      m = min(max(pl.blen, 0), n);
+      if (bslot <= p.null_id || bslot < 0 || bslot >= p.N) bslot = -1;
+    }
+  } else {
+    if (slot <= p.null_id || slot < 0 || slot >= p.N) return false;
+    n = min(max(p.commit_lens[b], 0), p.Q);
+    if (n == 0) return false;
+    f = p.final_slots ? p.final_slots[b] : slot;
+    if (f <= p.null_id || f < 0 || f >= p.N) return false;
+    if constexpr (ALIGN) {
+      bslot = p.bnd_slots[b];
+      m = min(max(p.bnd_lens[b], 0), n);
+      if (bslot <= p.null_id || bslot < 0 || bslot >= p.N) bslot = -1;
+    }
+  }
+  const int r = p.record_rows ? p.record_rows[b] : slot;
+  // The compaction's reads come next (after the record row, whose load is
+  // waited for at once), so that the record loads below retire after them
+  // and its writes can go out once those have landed.
+  std::conditional_t<STEP, HeadCompaction<D, C::NT>, NoCompaction<D, C::NT>>
+      conv;
+  conv.load(p, l, h, slot, n, f, bslot, m);
+  if (r < 0 || r >= p.R) {
+    conv.store(p);
+    return false;
   }
 
-  float* state = reinterpret_cast<float*>(p.state_base[l]);
+  float* state = global_addr<float>(p.state_base[l]);
   const int64_t sbs = p.state_bs[l];
   const float* src = state + int64_t(slot) * sbs + int64_t(h) * p.s_state_head;
   float* dst = state + int64_t(f) * sbs + int64_t(h) * p.s_state_head;
@@ -102,10 +245,10 @@ __device__ __forceinline__ bool commit_item(const CommitParams& p,
                 int64_t(h) * p.s_state_head;
 
   // Records of this head.
-  const float* corr = reinterpret_cast<const float*>(p.corr_base[l]) +
+  const float* corr = global_addr<const float>(p.corr_base[l]) +
                       int64_t(r) * p.corr_bs[l] + int64_t(h) * p.s_c_head;
   const int64_t kg_off = int64_t(r) * p.kg_bs[l] + int64_t(h) * p.s_kg_head;
-  const void* kg = reinterpret_cast<const void*>(p.kg_base[l]);
+  const void* kg = global_addr<const char>(p.kg_base[l]);
   const bool kg_bf16 = p.kg_bf16 != 0;
 
   // Small loads first (vector-memory counters retire in issue order): the
@@ -156,6 +299,7 @@ __device__ __forceinline__ bool commit_item(const CommitParams& p,
     const int t = j / D, v = j - t * D;
     if (j < QMAX * D) sm.cT[v * C::CS + t] = cv[jj];
   }
+  conv.store(p);
 #pragma unroll
   for (int t = 0; t < QMAX; ++t)
     dd[t] = (col_ok && t < n)
@@ -235,7 +379,7 @@ __device__ __forceinline__ bool commit_item(const CommitParams& p,
 }
 
 // One workgroup per item: blockIdx = (head, request, layer).
-template <int D, int QMAX, bool ALIGN>
+template <int D, int QMAX, bool ALIGN, bool STEP>
 __global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
     kda_commit_grid_kernel(CommitParams p) {
   __shared__ CommitSmem<D, QMAX, ALIGN> sm;
@@ -249,12 +393,13 @@ __global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
   const int l = item / per_layer;
   const int rem = item - l * per_layer;
   const int b = rem / p.H;
-  commit_item<D, QMAX, ALIGN>(p, sm, uniform(l), uniform(b), uniform(rem - b * p.H));
+  commit_item<D, QMAX, ALIGN, STEP>(p, sm, uniform(l), uniform(b),
+                                    uniform(rem - b * p.H));
 }
 
 // Persistent grid: workgroup g takes items g, g + gridDim.x, ... in
 // (layer, request, head) order, heads fastest.
-template <int D, int QMAX, bool ALIGN>
+template <int D, int QMAX, bool ALIGN, bool STEP>
 __global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
     kda_commit_strided_kernel(CommitParams p) {
   __shared__ CommitSmem<D, QMAX, ALIGN> sm;
@@ -266,31 +411,36 @@ __global__ void __launch_bounds__((CommitCfg<D, QMAX>::NT))
     const int b = uniform(rem / p.H);
     const int h = uniform(rem - b * p.H);
     // LDS is reused by the next item: wait until every thread is done.
-    if (commit_item<D, QMAX, ALIGN>(p, sm, l, b, h)) lds_barrier();
+    if (commit_item<D, QMAX, ALIGN, STEP>(p, sm, l, b, h)) lds_barrier();
   }
 }
 
-template <int D, int QMAX, bool ALIGN>
+template <int D, int QMAX, bool ALIGN, bool STEP>
 int launch_cqa(const CommitParams& p, hipStream_t stream) {
   using C = CommitCfg<D, QMAX>;
   const int64_t items = int64_t(p.L) * p.B * p.H;
   if (items > 0x7fffffff) return int(hipErrorInvalidValue);
   if (p.grid <= 0 && p.B <= 65535 && p.L <= 65535) {
-    hipLaunchKernelGGL((kda_commit_grid_kernel<D, QMAX, ALIGN>),
+    hipLaunchKernelGGL((kda_commit_grid_kernel<D, QMAX, ALIGN, STEP>),
                        dim3(p.H, p.B, p.L), dim3(C::NT), 0, stream, p);
   } else {
     const int64_t g = p.grid > 0 ? p.grid : 4096;
-    hipLaunchKernelGGL((kda_commit_strided_kernel<D, QMAX, ALIGN>),
+    hipLaunchKernelGGL((kda_commit_strided_kernel<D, QMAX, ALIGN, STEP>),
                        dim3(unsigned(g < items ? g : items)), dim3(C::NT), 0,
                        stream, p);
   }
   return int(hipGetLastError());
 }
 
+// Align mode when boundary slots are given (or, in the fused step, when the
+// plan has a block table).
 template <int D, int QMAX>
 int launch_cq(const CommitParams& p, hipStream_t stream) {
-  return p.bnd_slots ? launch_cqa<D, QMAX, true>(p, stream)
-                     : launch_cqa<D, QMAX, false>(p, stream);
+  if (p.step)
+    return p.plan.table ? launch_cqa<D, QMAX, true, true>(p, stream)
+                        : launch_cqa<D, QMAX, false, true>(p, stream);
+  return p.bnd_slots ? launch_cqa<D, QMAX, true, false>(p, stream)
+                     : launch_cqa<D, QMAX, false, false>(p, stream);
 }
 
 template <int D>

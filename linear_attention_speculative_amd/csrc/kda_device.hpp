@@ -67,6 +67,18 @@ __device__ __forceinline__ T& at(T* base, uint32_t off) {
                                off * uint32_t(sizeof(T)));
 }
 
+// A device address held as an integer (the per-layer address tables of the
+// commit) as a pointer known to point to global memory.  Going through the
+// global address space lets the compiler emit global memory instructions
+// for everything derived from it; a plain integer-to-pointer cast gives a
+// generic pointer and flat instructions, which also count against the LDS
+// wait counter, so that every LDS wait (a barrier) would wait for the
+// streaming loads as well.
+template <class T>
+__device__ __forceinline__ T* global_addr(int64_t a) {
+  return (T*)(__attribute__((address_space(1))) T*)(uintptr_t)a;
+}
+
 // Scalar loads of values the kernel never writes (per-request metadata,
 // per-head parameters) at wave-uniform addresses, with their own wait.
 // Written out because inside a persistent loop that also stores to global

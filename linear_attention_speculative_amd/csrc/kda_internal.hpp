@@ -55,6 +55,23 @@ constexpr int32_t kConvRow = 16;
 // mixed_qkv already holds the convolved q | k | v: no conv, no roll
 constexpr int32_t kNoConv = 64;
 
+// Commit plan of each request (one thread per request, or inline in the
+// fused commit step).
+struct PlanParams {
+  const int32_t* accepted;   // per request row
+  const int32_t* req_idx;    // [B] or null (row = b)
+  const int32_t* slots;      // [B]
+  const int32_t* qsl;        // [B + 1]
+  const int32_t* table;      // align mode, or null
+  int64_t s_tab_row, s_tab_col;
+  const int32_t* computed;   // per request row (align mode)
+  int32_t* lens;
+  int32_t* final_slots;
+  int32_t* bnd_slots;
+  int32_t* bnd_lens;
+  int32_t B, Q, null_id, block, rows, width;
+};
+
 struct CommitParams {
   const int64_t* state_base;  const int64_t* state_bs;
   const int64_t* corr_base;   const int64_t* corr_bs;
@@ -76,22 +93,14 @@ struct CommitParams {
   int64_t N, R;
   int32_t kg_bf16;
   int32_t grid;   // <= 0: one workgroup per item; > 0: persistent, strided
-};
-
-// Commit plan: one thread per request.
-struct PlanParams {
-  const int32_t* accepted;   // per request row
-  const int32_t* req_idx;    // [B] or null (row = b)
-  const int32_t* slots;      // [B]
-  const int32_t* qsl;        // [B + 1]
-  const int32_t* table;      // align mode, or null
-  int64_t s_tab_row, s_tab_col;
-  const int32_t* computed;   // per request row (align mode)
-  int32_t* lens;
-  int32_t* final_slots;
-  int32_t* bnd_slots;
-  int32_t* bnd_lens;
-  int32_t B, Q, null_id, block, rows, width;
+  // Fused commit step: every item plans its request inline (commit_lens,
+  // final_slots and bnd_* are then not read; the layer-0, head-0 item of a
+  // request writes the plan's outputs) and, with conv tables, copies its
+  // head's conv histories as the compaction does.
+  int32_t step;
+  int32_t conv_elem;            // bytes per conv-state element (2 or 4)
+  const int64_t* conv_tables;   // [4][L] as CompactParams::tables, or null
+  PlanParams plan;
 };
 
 // Conv-state compaction: one thread per (layer, request, channel).

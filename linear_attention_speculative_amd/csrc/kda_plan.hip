@@ -9,8 +9,7 @@
 // neither needs LDS or wide tiles; the compaction's grid puts consecutive
 // channels of one (request, layer) in one workgroup so the channel-strided
 // accesses of a dim-first state fall in neighbouring rows.
-#include "kda_device.hpp"
-#include "kda_internal.hpp"
+#include "kda_step.hpp"
 
 namespace kda {
 namespace {
@@ -22,29 +21,7 @@ __global__ void __launch_bounds__(kPlanThreads)
     kda_commit_plan_kernel(PlanParams p) {
   const int b = blockIdx.x * kPlanThreads + threadIdx.x;
   if (b >= p.B) return;
-  const int slot = p.slots[b];
-  const int row = p.req_idx ? p.req_idx[b] : b;
-  const int q = min(max(p.qsl[b + 1] - p.qsl[b], 0), p.Q);
-  int n = 0;
-  if (row >= 0 && row < p.rows && slot > p.null_id)
-    n = min(max(p.accepted[row], 0), q);
-  int final_slot = slot, bnd = p.null_id, blen = 0;
-  if (p.table && n > 0) {
-    const int64_t c = max(p.computed[row], 0);
-    const int64_t last = (c + n) / p.block;    // block of the next token
-    final_slot = last < p.width
-                     ? p.table[row * p.s_tab_row + last * p.s_tab_col]
-                     : p.null_id;
-    const int64_t start = last * p.block;
-    if (c < start && last - 1 < p.width) {     // the block before is full
-      bnd = p.table[row * p.s_tab_row + (last - 1) * p.s_tab_col];
-      blen = int(start - c);
-    }
-  }
-  p.lens[b] = n;
-  p.final_slots[b] = final_slot;
-  p.bnd_slots[b] = bnd;
-  p.bnd_lens[b] = blen;
+  store_plan(p, b, plan_request(p, b));
 }
 
 template <class T>
@@ -66,25 +43,17 @@ __global__ void __launch_bounds__(kCompactThreads)
   }
   if (ch >= p.C) return;
   const int64_t L = p.L;
-  T* base = reinterpret_cast<T*>(p.tables[l]);
+  T* base = global_addr<T>(p.tables[l]);
   const int64_t s_slot = p.tables[L + l];
   const int64_t s_ch = p.tables[2 * L + l];
   const int64_t s_tok = p.tables[3 * L + l];
   const T* src = base + slot * s_slot + ch * s_ch;
-  T hn[kConvWidth - 1], hb[kConvWidth - 1];
-#pragma unroll
-  for (int i = 0; i < kConvWidth - 1; ++i) {
-    hn[i] = src[(n - 1 + i) * s_tok];
-    hb[i] = bs >= 0 ? src[(m - 1 + i) * s_tok] : T{};
-  }
-  if (bs >= 0) {
-    T* dst = base + bs * s_slot + ch * s_ch;
-#pragma unroll
-    for (int i = 0; i < kConvWidth - 1; ++i) dst[i * s_tok] = hb[i];
-  }
-  T* dst = base + f * s_slot + ch * s_ch;
-#pragma unroll
-  for (int i = 0; i < kConvWidth - 1; ++i) dst[i * s_tok] = hn[i];
+  // everything is read before anything is written
+  const ConvHistory<T> hn = load_history(src, s_tok, n);
+  ConvHistory<T> hb{};
+  if (bs >= 0) hb = load_history(src, s_tok, m);
+  if (bs >= 0) store_history(base + bs * s_slot + ch * s_ch, s_tok, hb);
+  store_history(base + f * s_slot + ch * s_ch, s_tok, hn);
 }
 
 }  // namespace

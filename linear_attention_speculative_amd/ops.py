@@ -444,20 +444,41 @@ class CommitContext:
     def commit_step(self, num_accepted_tokens, state_indices, query_start_loc,
                     request_indices=None, block_table=None,
                     num_computed_tokens=None, mamba_block_size=None,
-                    record_rows=None, stream=None) -> tuple:
+                    record_rows=None, stream=None, fused=True,
+                    max_workgroups=0, out=None) -> tuple:
         """The ops page's `KDARecoverSSMCommitContext.commit`: plan, conv
         compaction (when the context has conv states), then the state
-        commit of every layer.  Returns the plan's four arrays."""
+        commit of every layer.  Returns the plan's four arrays.  fused:
+        all three in one launch (kda_recoverssm_commit_step); otherwise
+        three launches."""
         align = block_table is not None
+        if fused:
+            pa, out = self.plan_args(num_accepted_tokens, state_indices,
+                                     query_start_loc, request_indices,
+                                     block_table, num_computed_tokens,
+                                     mamba_block_size, out)
+            lens, final, bnd, blens = out
+            bnd_a, blens_a = (bnd, blens) if align else (None, None)
+            ca = self.args(state_indices, lens, final, record_rows,
+                           max_workgroups, bnd_a, blens_a)
+            xa = None if self.conv_tables is None else self.compact_args(
+                state_indices, lens, final, bnd_a, blens_a)
+            rc = _abi.load().kda_recoverssm_commit_step(
+                ctypes.byref(ca), ctypes.byref(pa),
+                None if xa is None else ctypes.byref(xa), _stream(stream))
+            if rc != _abi.KDA_OK:
+                _raise(rc)
+            return out
         lens, final, bnd, blens = self.plan(
             num_accepted_tokens, state_indices, query_start_loc,
             request_indices, block_table, num_computed_tokens,
-            mamba_block_size, stream=stream)
+            mamba_block_size, out=out, stream=stream)
         if self.conv_tables is not None:
             self.compact(state_indices, lens, final,
                          bnd if align else None, blens if align else None,
                          stream=stream)
         self.commit(state_indices, lens, final, record_rows, stream=stream,
+                    max_workgroups=max_workgroups,
                     boundary_state_indices=bnd if align else None,
                     boundary_recovery_lens=blens if align else None)
         return lens, final, bnd, blens

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_abi.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert kda.abi_version() == 3
+    assert kda.abi_version() == 4
     assert lib.kda_status_string(_abi.KDA_E_UNALIGNED) == b"KDA_E_UNALIGNED"
 
 
@@ -377,3 +377,64 @@ def test_compaction_and_boundary_checks():
                               spec_query_len=wl.Q)
     with pytest.raises(ValueError):
         plain.compact_args(si, lens)
+
+
+def test_commit_step_checks():
+    """The fused commit step takes the argument blocks of the three separate
+    calls, linked through the plan's outputs; anything else is refused."""
+    wl, ctx = _align_ctx()
+    lib = kda.load()
+    si, qsl = wl.state_indices, wl.query_start_loc
+    acc = wl.num_accepted_tokens
+    table = torch.zeros(wl.B, 5, dtype=torch.int32)
+    computed = torch.zeros(wl.B, dtype=torch.int32)
+
+    def blocks(align):
+        extra = dict(block_table=table, num_computed_tokens=computed,
+                     mamba_block_size=4) if align else {}
+        pa, out = ctx.plan_args(acc, si, qsl, **extra)
+        lens, fin, bnd, blen = out
+        b2 = (bnd, blen) if align else (None, None)
+        ca = ctx.args(si, lens, fin, None, 0, *b2)
+        xa = ctx.compact_args(si, lens, fin, *b2)
+        return pa, ca, xa, out
+
+    def code(ca, pa, xa):
+        return lib.kda_check_commit_step(
+            ctypes.byref(ca), ctypes.byref(pa),
+            None if xa is None else ctypes.byref(xa))
+
+    for align in (False, True):
+        pa, ca, xa, out = blocks(align)
+        assert code(ca, pa, xa) == 0
+        assert code(ca, pa, None) == 0               # no compaction
+    pa, ca, xa, (lens, fin, bnd, blen) = blocks(True)
+    # the commit must read the plan's outputs
+    other = torch.zeros_like(lens)
+    bad = ctx.args(si, other, fin, None, 0, bnd, blen)
+    assert code(bad, pa, xa) == _abi.KDA_E_ARG
+    bad = ctx.args(si, lens, fin)                    # align pair missing
+    assert code(bad, pa, xa) == _abi.KDA_E_ARG
+    bad = ctx.args(si.clone(), lens, fin, None, 0, bnd, blen)
+    assert code(bad, pa, xa) == _abi.KDA_E_ARG
+    # ... and so must the compaction
+    bad = ctx.compact_args(si, lens, None, bnd, blen)
+    assert code(ca, pa, bad) == _abi.KDA_E_ARG
+    bad = ctx.compact_args(si, lens, fin, bnd, blen)
+    bad.num_slots -= 1
+    assert code(ca, pa, bad) == _abi.KDA_E_ARG
+    bad = ctx.compact_args(si, lens, fin, bnd, blen)
+    bad.conv_dim -= 1
+    assert code(ca, pa, bad) == _abi.KDA_E_ARG
+    # one batch and window for all three
+    pa.spec_query_len = wl.Q - 1
+    assert code(ca, pa, xa) == _abi.KDA_E_ARG
+    # a non-align plan with a commit in align mode
+    pa, ca, xa, (lens, fin, bnd, blen) = blocks(False)
+    bad = ctx.args(si, lens, fin, None, 0, bnd, blen)
+    assert code(bad, pa, None) == _abi.KDA_E_ARG
+    # errors of the blocks themselves still come through
+    ca.num_layers = 0
+    assert code(ca, pa, xa) == _abi.KDA_E_ARG
+    assert lib.kda_check_commit_step(None, ctypes.byref(pa), None) == \
+        _abi.KDA_E_ARG

@@ -10,9 +10,11 @@ import torch
 import linear_attention_speculative_amd as kda
 import oracle
 from linear_attention_speculative_amd.debug import check_slot_aliasing
-from tests.gpu_check import TOL, bits, f64, rel_err
+from tests.gpu_check import (TOL, bits, check_verify, f64, rel_err,
+                             run_oracle_verify, snapshot)
 from workloads import drive, make_workload
-from workloads.gen import block_tables, step_activations
+from workloads.gen import (block_tables, running_block_tables,
+                           step_activations)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -249,3 +251,181 @@ def test_align_sequence_matches_oracle():
             assert np.array_equal(gpu[~w], oracle_in[l]["state"][~w])
         c = c + lens
     assert crossings >= 4
+
+
+# ---- the align workload at full size -------------------------------------------------
+
+def test_align_workload_sampled():
+    """The headline batch under prefix caching, in the launches the align
+    benchmark times: a two-block table per request (16 tokens per block),
+    the verify with accepted count 1, then plan, compaction and commit in
+    one call.  The plan is checked in full, bit for bit; a sample (every
+    request that crosses into its next block, and every eighth) against
+    the oracle: outputs and records, compacted conv histories bit for bit,
+    boundary and final states to the tolerance."""
+    wl = make_workload("headline", DEV)
+    assert wl.record_rows is None          # records indexed by source slot
+    L = wl.layers[0]
+    bs = 16
+    slots = _np(wl.state_indices)
+    table, computed = running_block_tables(slots, wl.N, bs, seed=5)
+    acc = _np(wl.commit_lens)
+    ref_plan = oracle.commit_plan(
+        num_accepted_tokens=acc, state_indices=slots,
+        query_start_loc=_np(wl.query_start_loc), spec_query_len=wl.Q,
+        block_table=table, num_computed_tokens=computed,
+        mamba_block_size=bs)
+    lens, final, bnd, blens = ref_plan
+    crossing = np.nonzero(bnd > 0)[0].tolist()
+    assert len(crossing) >= 10
+    reqs = sorted(set(range(0, wl.B, 8)) | set(crossing))
+
+    wl.num_accepted_tokens.fill_(1)        # the history was compacted
+    sample = snapshot(wl, 0, reqs)
+    live = [i for i, ok in enumerate(sample.valid) if ok]
+    # destinations that are no request's source: fresh blocks
+    dest = sorted(({int(final[b]) for b in reqs} |
+                   {int(bnd[b]) for b in reqs if bnd[b] > 0})
+                  - set(slots.tolist()))
+    dest_t = torch.tensor(dest, device=DEV)
+    dest_state = f64(L.state.index_select(0, dest_t))
+    dest_conv = f64(wl.conv_state_dim_first(0).index_select(0, dest_t))
+
+    ctx = drive.commit_context(wl, conv=True)
+    drive.verify(wl, 0, torch.zeros(1, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    ref = run_oracle_verify(sample)
+    errs = check_verify(wl, 0, sample, ref)      # before the compaction
+    plan = ctx.commit_step(wl.commit_lens, wl.state_indices,
+                           wl.query_start_loc, block_table=_i32(table),
+                           num_computed_tokens=_i32(computed),
+                           mamba_block_size=bs)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("lens", "final", "boundary", "blens"), plan,
+                          ref_plan):
+        assert np.array_equal(_np(g), r), name
+
+    # the compact pool: 0 null, then the sampled sources, then `dest`
+    n_src = sample.inputs["state"].shape[0]
+    cmap = {int(sample.slots[i]): int(sample.new_slot[i]) for i in live}
+    cmap.update({s: n_src + j for j, s in enumerate(dest)})
+
+    def compact(a):
+        return np.array([cmap[int(a[b])] if a[b] > 0 else 0 for b in reqs])
+
+    c_src, c_final, c_bnd = sample.new_slot, compact(final), compact(bnd)
+    conv_ref, = oracle.compact_conv_state(
+        conv_states=[np.concatenate([ref["conv_state"], dest_conv])],
+        state_indices=c_src, commit_lens=lens[reqs],
+        final_state_indices=c_final, boundary_state_indices=c_bnd,
+        boundary_recovery_lens=blens[reqs])
+    (new, written), = oracle.commit(
+        layers=[dict(state=np.concatenate([sample.inputs["state"],
+                                           dest_state]),
+                     correction=ref["correction"], key_gate=ref["key_gate"],
+                     A_log=sample.inputs["A_log"],
+                     dt_bias=sample.inputs["dt_bias"],
+                     use_lower_bound=L.use_lower_bound,
+                     lower_bound=L.lower_bound)],
+        state_indices=c_src, commit_lens=lens[reqs], spec_query_len=wl.Q,
+        final_state_indices=c_final, boundary_state_indices=c_bnd,
+        boundary_recovery_lens=blens[reqs])
+
+    inv = {c: s for s, c in cmap.items()}
+    pool = sorted(inv)
+    gpu_conv = f64(wl.conv_state_dim_first(0).index_select(
+        0, torch.tensor([inv[c] for c in pool], device=DEV)))
+    assert np.array_equal(gpu_conv, conv_ref[pool])
+    rows = np.nonzero(written.any(axis=1))[0]
+    assert written[c_bnd[c_bnd > 0]].all()
+    gpu = f64(L.state.index_select(
+        0, torch.tensor([inv[int(c)] for c in rows], device=DEV)))
+    err = rel_err(gpu, new[rows])
+    assert err <= TOL[wl.act], err
+    print("align full size", len(reqs), "requests,", len(crossing),
+          "boundaries, verify", errs, "state", err)
+
+
+# ---- the fused commit step ----------------------------------------------------------
+
+# name: (workload, sizes, align, conv states, request mapping, max_workgroups)
+STEP_CASES = {
+    "align_bf16_dimfirst": ("large", dict(D=32, Q=8, act="bf16",
+                                          conv_dim_first=True),
+                            True, True, False, 0),
+    "align_f32_tokfirst_mapped": ("large", dict(D=16, Q=4, act="f32",
+                                                conv_dim_first=False),
+                                  True, True, True, 0),
+    "align_noconv_d128_strided": ("large", dict(D=128, Q=4, act="bf16",
+                                                conv_dim_first=True),
+                                  True, False, False, 7),
+    "plain_conv_ragged_nulls": ("ragged", dict(D=64, Q=8, act="bf16",
+                                               conv_dim_first=True,
+                                               null_frac=0.2),
+                                False, True, False, 0),
+    "plain_noconv_q16_mapped": ("ragged", dict(D=128, Q=16, act="f32",
+                                               conv_dim_first=False),
+                                False, False, True, 0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(STEP_CASES))
+def test_fused_commit_step_matches_three_launches(case):
+    """kda_recoverssm_commit_step against kda_commit_plan, then
+    kda_compact_conv_state, then kda_recoverssm_commit on the same pools:
+    the plan's four arrays and every byte of every layer's pages (states,
+    conv states, records) are identical; the plan also equals the
+    oracle's."""
+    name, sizes, align, conv, mapped, max_wg = STEP_CASES[case]
+    rng = np.random.default_rng(80 + sorted(STEP_CASES).index(case))
+    B, width, bs = 24, 4, 8
+    rows = B + 3 if mapped else B
+    N = rows * width + 1 if align else 80
+    gates = [None, -5.0, None] if name == "large" else [None, -5.0]
+    wl = make_workload(name, DEV, B=B, H=2, N=N, weight=sizes["act"],
+                       gates=gates, **sizes)
+    Q = wl.Q
+    req = rng.permutation(rows)[:B] if mapped else None
+    acc = rng.integers(-1, Q + 2, size=rows)
+    extra, oextra = {}, {}
+    if align:
+        tables = block_tables(rows, width, N, seed=9)
+        computed = rng.integers(0, 2 * bs, size=rows)
+        ridx = req if mapped else np.arange(B)
+        src = tables[ridx, computed[ridx] // bs]
+        src[3] = 0                                   # a null request
+        wl.state_indices.copy_(_i32(src))
+        extra = dict(block_table=_i32(tables),
+                     num_computed_tokens=_i32(computed), mamba_block_size=bs)
+        oextra = dict(block_table=tables, num_computed_tokens=computed,
+                      mamba_block_size=bs)
+    if mapped:
+        extra["request_indices"] = _i32(req)
+        oextra["request_indices"] = req
+    counter = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for layer in range(len(wl.layers)):
+        drive.verify(wl, layer, counter)
+    ctx = drive.commit_context(wl, conv=conv)
+    args = (_i32(acc), wl.state_indices, wl.query_start_loc)
+    before = [L.page.clone() for L in wl.layers]
+    plan_f = [t.clone() for t in ctx.commit_step(
+        *args, fused=True, max_workgroups=max_wg, **extra)]
+    torch.cuda.synchronize()
+    after_f = [L.page.clone() for L in wl.layers]
+    for L, page in zip(wl.layers, before):
+        L.page.copy_(page)
+    plan_s = ctx.commit_step(*args, fused=False, **extra)
+    torch.cuda.synchronize()
+    ref = oracle.commit_plan(
+        num_accepted_tokens=acc, state_indices=_np(wl.state_indices),
+        query_start_loc=_np(wl.query_start_loc), spec_query_len=Q, **oextra)
+    for what, f, s, r in zip(("lens", "final", "boundary", "blens"), plan_f,
+                             plan_s, ref):
+        assert torch.equal(f, s), what
+        assert np.array_equal(_np(f), r), what
+    for layer, L in enumerate(wl.layers):
+        assert torch.equal(L.page, after_f[layer]), layer
+        assert not torch.equal(after_f[layer], before[layer]), layer
+    assert (ref[0] > 0).sum() >= 5
+    if align:
+        assert (ref[2] > 0).sum() >= 3

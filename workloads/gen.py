@@ -326,3 +326,24 @@ def block_tables(B: int, width: int, N: int, seed: int,
         raise ValueError("the pool is too small for the block tables")
     return rng.permutation(live)[:B * width].reshape(B, width) \
         .astype(np.int32)
+
+
+def running_block_tables(state_indices: np.ndarray, N: int, block_size: int,
+                         seed: int, null_block_id: int = 0):
+    """Two-block tables for a decode batch under prefix caching: column 0
+    is the request's current (running) state block, its source slot;
+    column 1 a free slot for the block after it (null once the free slots
+    run out).  Also draws the tokens already in the running block,
+    uniform in [0, block_size).  Returns (table int32 [B, 2], computed
+    int32 [B])."""
+    rng = np.random.default_rng(seed)
+    slots = np.asarray(state_indices)
+    B = slots.shape[0]
+    used = set(slots.tolist())
+    free = [s for s in range(null_block_id + 1, N) if s not in used]
+    table = np.full((B, 2), null_block_id, dtype=np.int32)
+    table[:, 0] = slots
+    nfree = min(len(free), B)
+    table[:nfree, 1] = free[:nfree]
+    computed = rng.integers(0, block_size, size=B).astype(np.int32)
+    return table, computed
