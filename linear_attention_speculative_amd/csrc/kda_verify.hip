@@ -725,7 +725,7 @@ __device__ __forceinline__ void null_item(const VerifyParams& p,
 // through LDS at the first barrier, after which `advance()` starts the
 // scalar loads of the next item's metadata.
 template <int D, int QMAX, bool ACT_BF16, bool FULL, bool FLUSH,
-          class Advance>
+          bool PERSISTENT, class Advance>
 __device__ __forceinline__ void verify_item(const VerifyParams& p,
                                             VerifySmem<D, QMAX>& sm,
                                             FlushSmem<D, QMAX, FLUSH>& fs,
@@ -789,8 +789,18 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
       const int t = j / D, k = j - t * D;
       if (t < q) s.gv[jj] = graw[t * p.s_g + k];
     }
-    s.bv = AT{};
-    if (tid < q) s.bv = rbeta[tid * p.s_beta];
+    // One workgroup per item: loaded by every lane (from a clamped, always
+    // valid position) rather than under `tid < q`.  A conditional load lets
+    // the compiler merge the sigmoid into its block, which then waits for
+    // every small load before the state tile is issued.  (The persistent
+    // loop keeps the conditional form: the other one costs it scalar
+    // registers, and it is not the default schedule.)
+    if constexpr (PERSISTENT) {
+      s.bv = AT{};
+      if (tid < q) s.bv = rbeta[tid * p.s_beta];
+    } else {
+      s.bv = rbeta[min(tid, q - 1) * p.s_beta];
+    }
   }
   // the state tile, in two halves (the second once the conv registers are
   // free)
@@ -868,10 +878,10 @@ __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
     };
     if (it.live) {
       if (it.q == QMAX)
-        verify_item<D, QMAX, ACT_BF16, true, false>(p, sm, nofs, it, drawn,
+        verify_item<D, QMAX, ACT_BF16, true, false, true>(p, sm, nofs, it, drawn,
                                                     buf, advance);
       else
-        verify_item<D, QMAX, ACT_BF16, false, false>(p, sm, nofs, it, drawn,
+        verify_item<D, QMAX, ACT_BF16, false, false, true>(p, sm, nofs, it, drawn,
                                                      buf,
                                               advance);
     } else {
@@ -918,10 +928,10 @@ __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
   auto advance = [] {};
   if (it.live) {
     if (it.q == QMAX)
-      verify_item<D, QMAX, ACT_BF16, true, FLUSH>(p, sm, fs, it, 0, 0,
+      verify_item<D, QMAX, ACT_BF16, true, FLUSH, false>(p, sm, fs, it, 0, 0,
                                                   advance);
     else
-      verify_item<D, QMAX, ACT_BF16, false, FLUSH>(p, sm, fs, it, 0, 0,
+      verify_item<D, QMAX, ACT_BF16, false, FLUSH, false>(p, sm, fs, it, 0, 0,
                                                    advance);
   } else {
     // Null block: zero outputs, touch no state, record or conv byte.
