@@ -236,6 +236,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ int fresh_tid() {
   int t = threadIdx.x;
   asm volatile("" : "+v"(t));
+  // the range survives the opaque copy: divisions by powers of two then
+  // need no sign fix-up (a value the compiler otherwise keeps, or spills)
+  __builtin_assume(t >= 0 && t < 1024);
   return t;
 }
 

@@ -77,11 +77,12 @@ struct VerifyCfg {
   static constexpr int PART = NB * D > D * DS ? NB * D : D * DS;
   static constexpr int JC = (3 * D + NT - 1) / NT;  // conv channels/thread
   static constexpr int JG = (QMAX * D + NT - 1) / NT;  // gate values/thread
-  // Register budget: 4 waves per SIMD up to Q = 4 (LDS allows 4
-  // workgroups per CU), 3 at Q = 8 (the most that fits without spills),
-  // 1 at Q = 16.  The ticket loop carries more live state: 3 up to Q = 4,
-  // 2 at Q = 8.  No instantiation may spill (the build checks it).
-  static constexpr int MIN_WAVES = QMAX >= 16 ? 1 : QMAX >= 8 ? 3 : 4;
+  // Register budget: 4 waves per SIMD up to Q = 8 (LDS allows 4
+  // workgroups per CU; at Q = 8 this needs the register savings of phases
+  // 1-3 below: 7% faster than 3 waves), 1 at Q = 16.  The ticket loop
+  // carries more live state: 3 up to Q = 4, 2 at Q = 8.  No instantiation
+  // may spill (the build checks it).
+  static constexpr int MIN_WAVES = QMAX >= 16 ? 1 : 4;
   static constexpr int TICKET_MIN_WAVES = QMAX >= 16 ? 1 : QMAX >= 8 ? 2 : 3;
   static_assert(RPP * PASSES == D, "tile rows");
   static_assert(CHUNKS * 4 * L == D, "tile columns");
@@ -422,6 +423,14 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
   }
 #pragma unroll
   for (int v0 = 0; v0 < C::NV; v0 += C::NB) {
+    // With several batches, each batch recomputes its products: opaque
+    // copies of the inputs keep the compiler from carrying shared partial
+    // products across the barrier in extra registers.
+    if constexpr (C::NV > C::NB) {
+#pragma unroll
+      for (int t = 0; t < QMAX; ++t)
+        asm volatile("" : "+v"(kk[t]), "+v"(qq[t]), "+v"(dd[t]));
+    }
     // this thread's share of scalars [v0, v0 + NB)
     auto put = [&](int idx, float val) {
       if (idx >= v0 && idx < v0 + C::NB && idx % C::NG == grp && col_ok)
@@ -469,14 +478,19 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
   };
   const float inv_sqrt_d = 1.0f / sqrtf(float(D));
   if (tid < D) {
+    // q, k and the decays are read again here (thread tid's own column),
+    // so that they need not stay in registers across phase 1's barriers
     float gam = 1.0f;
 #pragma unroll
     for (int t = 0; t < QMAX; ++t) {
-      gam *= dd[t];
+      const bool ok = t < q;
+      const float kt = ok ? sm.y[1][t][tid] : 0.0f;
+      const float qt = ok ? sm.y[0][t][tid] : 0.0f;
+      gam *= ok ? sm.dec[t][tid] : 1.0f;
       const float rk = rsqrtf(total(t) + kNormEps);
       const float rq = rsqrtf(total(QMAX + t) + kNormEps) * inv_sqrt_d;
-      sm.vec()[t][tid] = gam * kk[t] * rk;
-      sm.vec()[QMAX + t][tid] = gam * qq[t] * rq;
+      sm.vec()[t][tid] = gam * kt * rk;
+      sm.vec()[QMAX + t][tid] = gam * qt * rq;
     }
   }
   for (int j = tid; j < QMAX * QMAX; j += C::NT) {
@@ -508,31 +522,29 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
 #pragma unroll 1
   for (int t = 0; t < q; ++t) {
     {
-      f4 ka[C::CHUNKS], qa[C::CHUNKS];
-#pragma unroll
-      for (int c = 0; c < C::CHUNKS; ++c) {
-        const int cc = c * 4 * C::L + 4 * lg;
-        ka[c] = *reinterpret_cast<const f4*>(&sm.vec()[t][cc]);
-        qa[c] = *reinterpret_cast<const f4*>(&sm.vec()[QMAX + t][cc]);
-      }
+      // the key column, then the query column: one of them in registers at
+      // a time
       float acc[C::NVAL];
 #pragma unroll
-      for (int pp = 0; pp < C::PASSES; ++pp) {
-        float sa = 0.0f, sb = 0.0f;
+      for (int w = 0; w < 2; ++w) {
+        f4 va[C::CHUNKS];
 #pragma unroll
-        for (int c = 0; c < C::CHUNKS; ++c) {
-          const f4 s4 = st[pp][c];
-          sa = fmaf(s4.x, ka[c].x, sa);
-          sa = fmaf(s4.y, ka[c].y, sa);
-          sa = fmaf(s4.z, ka[c].z, sa);
-          sa = fmaf(s4.w, ka[c].w, sa);
-          sb = fmaf(s4.x, qa[c].x, sb);
-          sb = fmaf(s4.y, qa[c].y, sb);
-          sb = fmaf(s4.z, qa[c].z, sb);
-          sb = fmaf(s4.w, qa[c].w, sb);
+        for (int c = 0; c < C::CHUNKS; ++c)
+          va[c] = *reinterpret_cast<const f4*>(
+              &sm.vec()[w * QMAX + t][c * 4 * C::L + 4 * lg]);
+#pragma unroll
+        for (int pp = 0; pp < C::PASSES; ++pp) {
+          float sa = 0.0f;
+#pragma unroll
+          for (int c = 0; c < C::CHUNKS; ++c) {
+            const f4 s4 = st[pp][c];
+            sa = fmaf(s4.x, va[c].x, sa);
+            sa = fmaf(s4.y, va[c].y, sa);
+            sa = fmaf(s4.z, va[c].z, sa);
+            sa = fmaf(s4.w, va[c].w, sa);
+          }
+          acc[2 * pp + w] = sa;
         }
-        acc[2 * pp] = sa;
-        acc[2 * pp + 1] = sb;
       }
       dslot[t] = transpose_sum<C::L, C::NVAL>(acc, lg);
     }
