@@ -365,6 +365,9 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
       (Lc * ea) % 4 == 0 && (s_chan * ea) % 4 == 0 &&
       (cs.stride[0] * ea) % 4 == 0)
     p.flags |= kda::kConvRow;
+  if (conv && cw.stride[1] == 1 && cw.stride[0] == kda::kConvWidth &&
+      aligned(cw.data, uintptr_t(kda::kConvWidth) * elem_size(cw.dtype)))
+    p.flags |= kda::kWRow;
   p.lb = a->lower_bound;
   p.n_items = int32_t(int64_t(a->batch) * H);
   p.per_ticket = a->items_per_ticket;

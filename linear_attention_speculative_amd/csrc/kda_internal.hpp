@@ -54,6 +54,9 @@ constexpr int32_t kLowerBound = 8;
 constexpr int32_t kConvRow = 16;
 // mixed_qkv already holds the convolved q | k | v: no conv, no roll
 constexpr int32_t kNoConv = 64;
+// each channel's four taps are contiguous and their row is aligned to its
+// size (8 bytes in bf16, 16 in fp32): read with one load per channel
+constexpr int32_t kWRow = 128;
 
 // Commit plan of each request (one thread per request, or inline in the
 // fused commit step).

@@ -215,13 +215,30 @@ __device__ __forceinline__ void load_head(const VerifyParams& p, int h,
     const int j = tid + jj * C::NT;
     if (conv && j < 3 * D) {
       const int part = j / D, d = j - part * D;
-      const uint32_t wo = (part * HD + h * D + d) * p.s_w_chan;
+      const uint32_t ch = part * HD + h * D + d;
+      if (p.flags & kWRow) {
+        // the channel's taps in one load; bf16 taps stay packed two per
+        // word until they are used
+        if (w_bf16) {
+          const uint2 v = at(static_cast<const uint2*>(p.conv_weight), ch);
+          hr.w[jj][0] = v.x;
+          hr.w[jj][1] = v.y;
+        } else {
+          const uint4 v = at(static_cast<const uint4*>(p.conv_weight), ch);
+          hr.w[jj][0] = v.x;
+          hr.w[jj][1] = v.y;
+          hr.w[jj][2] = v.z;
+          hr.w[jj][3] = v.w;
+        }
+      } else {
+        const uint32_t wo = ch * p.s_w_chan;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t o = wo + i * p.s_w_tap;
-        hr.w[jj][i] =
-            w_bf16 ? uint32_t(at(static_cast<const uint16_t*>(p.conv_weight), o))
-                   : at(static_cast<const uint32_t*>(p.conv_weight), o);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t o = wo + i * p.s_w_tap;
+          hr.w[jj][i] =
+              w_bf16 ? uint32_t(at(static_cast<const uint16_t*>(p.conv_weight), o))
+                     : at(static_cast<const uint32_t*>(p.conv_weight), o);
+        }
       }
     }
   }
@@ -299,9 +316,17 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
       const int part = j / D, d = j - part * D;
       const int ch = part * HD + h * D + d;
       float w[4];
+      if (w_bf16 && (p.flags & kWRow)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = __uint_as_float(w_bf16 ? hr.w[jj][i] << 16 : hr.w[jj][i]);
+        for (int i = 0; i < 2; ++i) {
+          w[2 * i] = __uint_as_float(hr.w[jj][i] << 16);
+          w[2 * i + 1] = __uint_as_float(hr.w[jj][i] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = __uint_as_float(w_bf16 ? hr.w[jj][i] << 16 : hr.w[jj][i]);
+      }
       // history: positions a-1 .. a+1 of the conv state
       AT h0 = s.hist[jj][0], h1 = s.hist[jj][1], h2 = s.hist[jj][2];
       if (row_fast) {
