@@ -75,3 +75,30 @@ def test_algorithmic_bytes_match_a_per_tensor_count():
                 got["compact"]) == (v, c, fl, cp), name
         qsl = wl.query_start_loc.numpy()
         assert got["tokens"] == int(np.minimum(np.diff(qsl), wl.Q).sum())
+
+
+def test_running_block_tables():
+    """The align workload's tables: column 0 is each request's source slot,
+    column 1 a free slot no source uses (distinct across requests, null once
+    the free slots run out); the tokens already in the running block lie in
+    [0, block size)."""
+    from workloads.gen import running_block_tables
+    wl = make_workload("headline")
+    src = wl.state_indices.numpy()
+    table, computed = running_block_tables(src, wl.N, 16, seed=5)
+    assert table.dtype == np.int32 and table.shape == (wl.B, 2)
+    assert np.array_equal(table[:, 0], src)
+    nxt = table[:, 1]
+    live = nxt[nxt > 0]
+    assert len(set(live.tolist())) == len(live)
+    assert not set(live.tolist()) & set(src.tolist())
+    assert live.max() < wl.N
+    assert len(live) == min(wl.B, wl.N - 1 - len(set(src.tolist())))
+    assert computed.min() >= 0 and computed.max() < 16
+    # the same seed gives the same tables
+    t2, c2 = running_block_tables(src, wl.N, 16, seed=5)
+    assert np.array_equal(t2, table) and np.array_equal(c2, computed)
+    # with too few free slots, the last rows' next block is null
+    small, _ = running_block_tables(np.arange(1, 9), 12, 16, seed=1)
+    assert small[:3, 1].tolist() == [9, 10, 11]
+    assert (small[3:, 1] == 0).all()
