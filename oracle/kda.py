@@ -7,7 +7,7 @@ inputs.  Values that the GPU stores in a narrower type and that a later
 stage reads back (records, committed states) are rounded to that storage type
 with round-to-nearest-even, as the storage itself would do.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * The null block id is an argument; a slot <= it, or past the pool, is null.
   * The convolution history sits at offset (accepted - 1) of a conv state of
     length Q + W - 2; the roll writes the W - 2 newest history entries
