@@ -366,6 +366,11 @@ STEP_CASES = {
     "plain_noconv_q16_mapped": ("ragged", dict(D=128, Q=16, act="f32",
                                                conv_dim_first=False),
                                 False, False, True, 0),
+    # the pages' record layout: the key record in the activation dtype
+    "align_bf16_keyrecord_d64": ("large", dict(D=64, Q=4, act="bf16",
+                                               conv_dim_first=True,
+                                               kg_dtype="act"),
+                                 True, True, False, 0),
 }
 
 
