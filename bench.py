@@ -40,10 +40,22 @@ Other workloads (`--workload`), each one JSON line of the same form:
   fused     the headline batch in the deferred form: each step is one
             launch that folds the previous step's accepted positions into
             the checkpoints and then verifies (the same verify and commit
-            work per step, one state pass fewer).
+            work per step, one state pass fewer);
+  tiny      2 requests, 2 heads, head dim 16, Q=3, fp32: `value` is the CPU
+            seconds of one oracle pass (verify + commit of the whole
+            workload); the GPU step time is reported beside it;
+  single    one request at the full head shape (B=1, token-first conv):
+            launch-latency bound, so the absolute microseconds per
+            verify + commit are the figure (graph-replayed and eager);
+  ragged    64 requests with ragged windows (q uniform in 1..4) and 10%
+            null slots, verify only; its state (about 116 MiB) fits the
+            256 MB last-level cache, so every timed launch follows an
+            untimed 1 GiB write that evicts it.
 The default run (headline) is the one the throughput figure is quoted on.
+`--cold-steps` times any workload that way (an evicting write before every
+timed step, events around the step's launches only).
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold-steps]
   python bench.py --copy-calibration   # plain copy for HBM counter scaling
 """
 from __future__ import annotations
@@ -59,10 +71,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+METRIC = ("verified tokens/s + % HBM peak (KDA verify+commit, H=32 K=V=128, "
+          "Q=4)")
+EVICT_BYTES = 1 << 30          # the cache-evicting write before cold steps
+# workloads whose every timed launch is cold (the state fits the caches)
+COLD_WORKLOADS = ("ragged",)
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 ALIGN_BLOCK_SIZE = 16          # tokens per state block, align workload
 KERNEL_SOURCES = {
     "kda_verify_grid_kernel": "kda_verify.hip",
+    "kda_verify_vtile_kernel": "kda_verify.hip",
+    "kda_verify_kernel": "kda_verify.hip",
     "kda_commit_grid_kernel": "kda_commit.hip",
 }
 
@@ -133,13 +152,32 @@ def algorithmic_bytes(wl, pending=None, boundary=None) -> dict:
                 compact=compact)
 
 
-def build_phases(name, wl, drive, torch):
+SCHEDULES = {"default": 0, "per-item": 1, "tickets": 2, "v-tiles": 3}
+
+
+def verify_kernel(wl, schedule: int, v_tiles: int) -> str:
+    """Name of the kernel the plain verify of `wl` launches: V-tiles when
+    asked for, or by default (the library's rule, given a counter with one
+    arrival slot per item) for head dims 64/128, windows up to 8 and at most
+    256 (request, head) items; else one workgroup per item."""
+    if schedule == SCHEDULES["v-tiles"]:
+        return "kda_verify_vtile_kernel"
+    if schedule == SCHEDULES["tickets"]:
+        return "kda_verify_kernel"
+    if (schedule == 0 and wl.D in (64, 128) and wl.Q <= 8 and
+            (v_tiles > 1 or wl.B * wl.H <= 256)):
+        return "kda_verify_vtile_kernel"
+    return "kda_verify_grid_kernel"
+
+
+def build_phases(name, wl, drive, torch, schedule=0, v_tiles=0):
     """The launches of one step of workload `name`, as phases timed with
     events on both sides: (kernel, algorithmic bytes per step, launches per
     step, function).  Returns (phases, verified tokens per step, config
     note)."""
     import numpy as np
-    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # ticket counter + one arrival counter per (request, head)
+    counter = drive.counter(wl)
     L = len(wl.layers)
     if name in ("deferred", "fused"):
         nb = algorithmic_bytes(wl, pending=wl.commit_lens.cpu().numpy())
@@ -182,15 +220,24 @@ def build_phases(name, wl, drive, torch):
                 f"layers=1 align bs={bs}, {int((boundary > 0).sum())} "
                 "boundaries per step, fused commit step")
     nb = algorithmic_bytes(wl)
+    vname = verify_kernel(wl, schedule, v_tiles)
 
     def verify_all():
         for layer in range(L):
-            drive.verify(wl, layer, counter)
+            drive.verify(wl, layer, counter, schedule=schedule,
+                         v_tiles=v_tiles)
+
+    if name == "ragged":
+        # verify only; the commit of this batch is exercised by the tests
+        return ([(vname, nb["verify"] * L, L,
+                  verify_all)], nb["tokens"] * L,
+                f"layers={L} verify only, {int((wl.state_indices == 0).sum())} "
+                "null slots")
 
     def commit():
         ctx.commit(wl.state_indices, wl.commit_lens,
                    record_rows=wl.record_rows)
-    return ([("kda_verify_grid_kernel", nb["verify"] * L, L, verify_all),
+    return ([(vname, nb["verify"] * L, L, verify_all),
              ("kda_commit_grid_kernel", nb["commit"] * L, 1, commit)],
             nb["tokens"] * L, f"layers={L}")
 
@@ -208,48 +255,92 @@ def traffic_from_profiles(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_threads() -> dict:
+    """CPU threads this process may use, and the BLAS thread setting numpy
+    would use by default (before the one-thread limit below)."""
+    info = {"host_cores": len(os.sched_getaffinity(0))}
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas"] = [{"api": p.get("internal_api"),
+                         "num_threads": p.get("num_threads")}
+                        for p in threadpool_info()]
+    except ImportError:  # pragma: no cover
+        info["blas"] = None
+    return info
+
+
+def _one_thread():
+    import contextlib
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        return contextlib.nullcontext()
+
+
+def _oracle_pass(wl, reqs, oracle, snapshot):
+    """Oracle verify + commit of layer 0 for `reqs`; returns (seconds spent
+    in the oracle, verified tokens)."""
+    L = wl.layers[0]
+    lens = wl.commit_lens.cpu().numpy()
+    sample = snapshot(wl, 0, reqs)
+    t0 = time.perf_counter()
+    ref = oracle.conv_update_verify(**sample.inputs)
+    oracle.commit(layers=[dict(
+        state=sample.inputs["state"], correction=ref["correction"],
+        key_gate=ref["key_gate"], A_log=sample.inputs["A_log"],
+        dt_bias=sample.inputs["dt_bias"],
+        use_lower_bound=L.use_lower_bound, lower_bound=L.lower_bound)],
+        state_indices=sample.new_slot, commit_lens=lens[reqs],
+        spec_query_len=wl.Q,
+        record_rows=None if wl.record_rows is None else sample.new_row)
+    spent = time.perf_counter() - t0
+    return spent, sum(min(len(t), wl.Q) for t in sample.tok)
+
+
 def cpu_baseline(wl, seconds: float, max_passes: int = 8) -> dict:
     """The fp64 oracle, as it stands, single-threaded, on the requests of
     the same workload taken in order, 16 at a time (verify + commit), until
     `seconds` of CPU time have passed; passes over the whole batch repeat
     (at most `max_passes`) when one pass takes less than that."""
-    import contextlib
-    try:
-        from threadpoolctl import threadpool_limits
-        limit = threadpool_limits(limits=1)
-    except ImportError:  # pragma: no cover
-        limit = contextlib.nullcontext()
     import oracle
     from workloads.sample import snapshot
-    L = wl.layers[0]
-    lens = wl.commit_lens.cpu().numpy()
     tokens, spent, done = 0, 0.0, 0
-    with limit:
+    with _one_thread():
         while spent < seconds and done < wl.B * max_passes:
             start = done % wl.B
             reqs = list(range(start, min(start + 16, wl.B)))
-            sample = snapshot(wl, 0, reqs)
-            t0 = time.perf_counter()
-            ref = oracle.conv_update_verify(**sample.inputs)
-            oracle.commit(layers=[dict(
-                state=sample.inputs["state"], correction=ref["correction"],
-                key_gate=ref["key_gate"], A_log=sample.inputs["A_log"],
-                dt_bias=sample.inputs["dt_bias"],
-                use_lower_bound=L.use_lower_bound,
-                lower_bound=L.lower_bound)],
-                state_indices=sample.new_slot, commit_lens=lens[reqs],
-                spec_query_len=wl.Q,
-                record_rows=None if wl.record_rows is None
-                else sample.new_row)
-            spent += time.perf_counter() - t0
-            tokens += sum(min(len(t), wl.Q) for t in sample.tok)
+            dt, tok = _oracle_pass(wl, reqs, oracle, snapshot)
+            spent += dt
+            tokens += tok
             done += len(reqs)
-    return {"value": tokens / spent, "unit": "verified tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} request verifies + commits "
-                      f"({done / wl.B:.2f} passes over the {wl.B}-request "
-                      f"batch), {tokens} tokens in {spent:.1f} s, numpy "
-                      "fp64, 1 thread"}
+    return dict({"value": tokens / spent, "unit": "verified tokens/s",
+                 "cores": 1, "kind": "oracle",
+                 "sample": f"{done} request verifies + commits "
+                           f"({done / wl.B:.2f} passes over the {wl.B}-request "
+                           f"batch), {tokens} tokens in {spent:.1f} s, numpy "
+                           "fp64, 1 thread (BLAS limited to 1)"},
+                **host_threads())
+
+
+def oracle_seconds(wl, seconds: float = 3.0) -> dict:
+    """CPU seconds of one oracle pass over the whole workload (verify +
+    commit of every request), single-threaded: median over repeated passes
+    until `seconds` have passed (at least 5)."""
+    import oracle
+    from workloads.sample import snapshot
+    times, tok = [], 0
+    with _one_thread():
+        while sum(times) < seconds or len(times) < 5:
+            dt, tok = _oracle_pass(wl, list(range(wl.B)), oracle, snapshot)
+            times.append(dt)
+    times.sort()
+    return dict({"value": times[len(times) // 2], "unit": "s", "cores": 1,
+                 "kind": "oracle", "passes": len(times),
+                 "min_s": times[0], "max_s": times[-1],
+                 "sample": f"the whole workload ({wl.B} requests, {tok} "
+                           "tokens) per pass, numpy fp64, 1 thread"},
+                **host_threads())
 
 
 def copy_calibration(gib: float = 1.0, reps: int = 5) -> None:
@@ -279,6 +370,15 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true",
                     help="time the K steps as eager launches, not as one "
                          "replay of a HIP graph holding them")
+    ap.add_argument("--schedule", default="default", choices=list(SCHEDULES),
+                    help="verify schedule of the headline-form workloads")
+    ap.add_argument("--v-tiles", type=int, default=0,
+                    help="workgroups per (request, head) for --schedule "
+                         "v-tiles (0: the library's choice)")
+    ap.add_argument("--cold-steps", action="store_true",
+                    help="precede every timed step with an untimed 1 GiB "
+                         "write that evicts the caches; the step time is "
+                         "then taken from events around its launches")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -298,8 +398,15 @@ def main() -> int:
     cfg_name = "headline" if args.workload in ("align", "fused") \
         else args.workload
     wl = make_workload(cfg_name, "cuda", out_dtype="act")
-    phases, tokens, note = build_phases(args.workload, wl, drive, torch)
+    phases, tokens, note = build_phases(args.workload, wl, drive, torch,
+                                        SCHEDULES[args.schedule],
+                                        args.v_tiles)
+    if args.schedule != "default" or args.v_tiles:
+        note += f" verify schedule={args.schedule} v_tiles={args.v_tiles}"
     P = len(phases)
+    cold_steps = args.cold_steps or args.workload in COLD_WORKLOADS
+    evict = torch.empty(EVICT_BYTES // 4, dtype=torch.float32,
+                        device="cuda") if cold_steps else None
 
     def step(ev=None):
         for i, (_, _, _, fn) in enumerate(phases):
@@ -319,10 +426,15 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if evict is not None:
+            evict.fill_(float(k))          # untimed: before the first event
         step(events[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    if evict is not None:
+        # cold steps: the time between each step's first and last event
+        ms_step = sum(e[0].elapsed_time(e[P]) for e in events) / args.steps
     # per phase: microseconds per launch (a phase of n launches / n)
     per = [sorted(e[i].elapsed_time(e[i + 1]) * 1e3 / phases[i][2]
                   for e in events) for i in range(P)]
@@ -336,8 +448,8 @@ def main() -> int:
     # replayed once (after an untimed replay), so that host launch overhead
     # stays out of the step time.  Falls back to the eager time if the
     # capture fails.
-    timing, ms_eager = "eager", ms_step
-    if not args.eager:
+    timing, ms_eager = ("cold" if evict is not None else "eager"), ms_step
+    if not args.eager and evict is None:
         try:
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
@@ -420,7 +532,8 @@ def main() -> int:
     traffic = traffic_from_profiles(kname, args.workload)
     step_bytes = sum(ph[1] for ph in phases)
     result = {
-        "metric": "verified tokens/s (KDA verify+commit, H=32 K=V=128, Q=4)",
+        "metric": METRIC if args.workload == "headline" else
+        f"verified tokens/s ({args.workload} workload)",
         "value": tokens / (ms_step * 1e-3),
         "unit": "verified tokens/s",
         "n_gpus": 1,
@@ -435,6 +548,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic (seeded decode batch, bf16 activations, fp32 "
                 "state)",
+        "us_per_step": ms_step * 1e3,
         "config": {"workload": f"{args.workload}: B={wl.B} H={wl.H} "
                                f"K=V={wl.D} Q={wl.Q} {note} "
                                f"pool={wl.N} slots "
@@ -445,7 +559,15 @@ def main() -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kname, "bytes_per_launch": by,
-                     "us_per_launch": ms * 1e3},
+                     "us_per_launch": ms * 1e3,
+                     # the same kernel launched after an untimed 1 GiB
+                     # write that evicts the caches (median of --cold)
+                     "cold": None if not cold[dom] else {
+                         "us_per_launch": quant(cold[dom], 0.5),
+                         "achieved": by / (quant(cold[dom], 0.5) * 1e-6)
+                         / 1e9,
+                         "frac": by / (quant(cold[dom], 0.5) * 1e-6) / 1e9
+                         / HBM_PEAK_GBS}},
         "step_hbm": dict(
             {"bytes": step_bytes,
              "GB/s": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -488,7 +610,16 @@ def main() -> int:
             "frac": fby / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         print(f"# deferred form: {fms:.4f} ms/step", file=sys.stderr,
               flush=True)
-    if args.cpu_seconds > 0:
+    if args.workload == "tiny":
+        # the small workload's figure is the oracle's CPU time; the GPU
+        # step time stays beside it
+        cpu = oracle_seconds(wl)
+        result.update(metric="CPU seconds of one oracle pass (tiny workload: "
+                             "verify + commit)",
+                      value=cpu["value"], unit="s", higher_is_better=False,
+                      dtype="f64", gpu_verified_tokens_per_s=result["value"])
+        result["cpu_baseline"] = cpu
+    elif args.cpu_seconds > 0:
         print("# cpu baseline ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)

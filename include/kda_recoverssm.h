@@ -48,8 +48,8 @@
  *    may be captured in a HIP graph.
  *  - Every entry point returns KDA_OK (0) or a kda_status code; a failing
  *    call launches nothing and leaves a message for kda_last_error() in the
- *    calling thread.  Zero-sized work (batch 0 or no tokens) returns KDA_OK
- *    without launching.
+ *    calling thread.  Zero-sized work (batch 0, or no tokens for a verify
+ *    without pending_lens) returns KDA_OK without launching.
  *  - Values that live on the device (query lengths, slots, accepted counts,
  *    commit lengths, record rows) are never read by the host.  The kernels
  *    clamp them instead: query length to [0, Q], accepted count to [1, Q],
@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 /* Status codes. */
 typedef enum {
@@ -102,9 +102,19 @@ typedef enum {
   KDA_SCHEDULE_PER_ITEM = 1,   /* one workgroup per item, handed out by the
                                   hardware dispatcher (each XCD takes one
                                   contiguous eighth of the items) */
-  KDA_SCHEDULE_TICKETS = 2     /* persistent workgroups drawing tickets of
+  KDA_SCHEDULE_TICKETS = 2,    /* persistent workgroups drawing tickets of
                                   items_per_ticket items from work_counter
                                   (the kernels page's design) */
+  KDA_SCHEDULE_V_TILES = 3     /* v_tiles workgroups per item, each taking
+                                  head_dim / v_tiles rows of the state (the
+                                  ops page's verify grid over V blocks,
+                                  requests and heads), for batches too small
+                                  to fill the GPU; the conv roll of the q
+                                  and k channels waits for every V-tile of
+                                  the item through an arrival counter in
+                                  work_counter.  Head dims 64 and 128,
+                                  windows up to 8, no pending_lens.  Same
+                                  results, bit for bit, as PER_ITEM. */
 } kda_schedule;
 
 /* A strided tensor view.  `stride` is in elements; unused trailing entries
@@ -146,11 +156,14 @@ typedef struct {
   const int32_t* num_accepted_tokens;  /* [batch] conv history offset + 1 */
   const int32_t* record_rows;          /* [batch] record row, or NULL: the
                                           request's state slot */
-  int32_t* work_counter;   /* device int32[1]: ticket counter of the ticket
-                              schedule.  Must be 0 before the first launch;
-                              every launch leaves it at 0.  One counter per
-                              launch in flight.  May be NULL for the other
-                              schedules. */
+  int32_t* work_counter;   /* device int32[work_counter_len]: [0] is the
+                              ticket counter of the ticket schedule,
+                              [1 + b * H + h] the arrival counter of request
+                              b, head h under the V-tile schedule (fused
+                              conv only).  Must be 0 before the first
+                              launch; every launch leaves it at 0.  One
+                              counter array per launch in flight.  May be
+                              NULL for the other schedules. */
   int32_t batch;
   int32_t spec_query_len;  /* Q */
   int32_t null_block_id;   /* slots <= this are null (the ops page imports
@@ -174,8 +187,17 @@ typedef struct {
                               are folded into its checkpoint, which is
                               written back in place, and the verify then
                               starts from the updated state and overwrites
-                              that row with this step's records.  Uses the
-                              per-item schedule (batch <= 65535). */
+                              that row with this step's records.  A request
+                              with a live slot and an empty window (no
+                              tokens, or T = 0) still folds its pending
+                              positions.  Uses the per-item schedule
+                              (batch <= 65535). */
+  int32_t work_counter_len; /* elements of work_counter; 0 with a counter
+                               means 1.  The V-tile schedule of the fused
+                               conv verify needs 1 + batch * H (the default
+                               schedule only picks V-tiles when it is). */
+  int32_t v_tiles;         /* V-tile schedule: 2, 4 or 8 workgroups per
+                              (request, head); 0 = the library's choice */
 } kda_verify_args;
 
 /* Arguments of kda_recoverssm_commit.  Per-layer tensors are described by

@@ -23,6 +23,7 @@ KDA_E_ARG = 8
 KDA_SCHEDULE_DEFAULT = 0
 KDA_SCHEDULE_PER_ITEM = 1
 KDA_SCHEDULE_TICKETS = 2
+KDA_SCHEDULE_V_TILES = 3
 
 KDA_F32 = 0
 KDA_BF16 = 1
@@ -60,6 +61,7 @@ class KdaVerifyArgs(Structure):
         ("max_workgroups", c_int32), ("items_per_ticket", c_int32),
         ("schedule", c_int32),
         ("pending_lens", c_void_p),
+        ("work_counter_len", c_int32), ("v_tiles", c_int32),
     ]
 
 

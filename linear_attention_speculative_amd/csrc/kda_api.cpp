@@ -77,6 +77,14 @@ struct VerifyPlan {
   int schedule = 0;
 };
 
+// V-tiles per (request, head) item that the default schedule uses for
+// `items` items (1: whole items): enough workgroups to cover the compute
+// units when the items alone would not.  `floor`: the least value returned.
+int default_vtiles(int64_t items, int floor) {
+  int vt = items <= 64 ? 8 : items <= 128 ? 4 : items <= 256 ? 2 : 1;
+  return vt < floor ? floor : vt;
+}
+
 #define KDA_TRY(expr)             \
   do {                            \
     int rc_ = (expr);             \
@@ -269,8 +277,14 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
     return fail(KDA_E_ARG, "items_per_ticket is negative");
   if (a->max_workgroups < 0)
     return fail(KDA_E_ARG, "max_workgroups is negative");
-  if (a->schedule < KDA_SCHEDULE_DEFAULT || a->schedule > KDA_SCHEDULE_TICKETS)
+  if (a->schedule < KDA_SCHEDULE_DEFAULT || a->schedule > KDA_SCHEDULE_V_TILES)
     return fail(KDA_E_ARG, "unknown schedule %d", a->schedule);
+  if (a->work_counter_len < 0)
+    return fail(KDA_E_ARG, "work_counter_len is negative");
+  if (a->v_tiles != 0 && a->v_tiles != 2 && a->v_tiles != 4 &&
+      a->v_tiles != 8)
+    return fail(KDA_E_ARG, "v_tiles must be 0, 2, 4 or 8 (got %d)",
+                a->v_tiles);
   if (a->batch > 0) {
     if (!a->query_start_loc || !a->state_indices ||
         (conv && !a->num_accepted_tokens))
@@ -312,6 +326,14 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
       Q * (a->correction.stride[2] + a->key_gate.stride[2]) + 2 * D >
           i32max)
     return fail(KDA_E_LAYOUT, "per-request offsets exceed 2^31 elements");
+  // The out, correction and conv-tap accesses form their in-item offsets
+  // in BYTES as unsigned 32-bit values from a wave-uniform base: bound
+  // those byte offsets too (2^31, as the element offsets above).
+  const int ew = conv ? elem_size(cw.dtype) : 0;
+  if ((Q * a->out.stride[0] + D) * eo > i32max ||
+      (Q * a->correction.stride[2] + D) * 4 > i32max ||
+      (C3 * cw.stride[0] + kda::kConvWidth * cw.stride[1]) * ew > i32max)
+    return fail(KDA_E_LAYOUT, "per-request byte offsets exceed 2^31");
 
   kda::VerifyParams& p = plan->p;
   p = kda::VerifyParams{};
@@ -371,11 +393,46 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
   p.lb = a->lower_bound;
   p.n_items = int32_t(int64_t(a->batch) * H);
   p.per_ticket = a->items_per_ticket;
+
+  // V-tiles: possible for head dims 64 and 128 and windows up to 8 without
+  // the deferred flush; the fused conv needs one arrival counter per item.
+  const int64_t counter_len =
+      a->work_counter == nullptr ? 0
+                                 : (a->work_counter_len > 0 ? a->work_counter_len
+                                                            : 1);
+  const int64_t items = int64_t(a->batch) * H;
+  const bool vt_shape = (D == 64 || D == 128) && Q <= 8 &&
+                        a->pending_lens == nullptr;
+  const bool vt_counter = !conv || counter_len >= 1 + items;
+  int schedule = a->schedule;
+  int vt = a->v_tiles;
+  if (schedule == KDA_SCHEDULE_V_TILES) {
+    if (!vt_shape)
+      return fail(KDA_E_UNSUPPORTED,
+                  "the V-tile schedule supports head dims 64 and 128, "
+                  "windows up to 8 and no pending_lens");
+    if (!vt_counter)
+      return fail(KDA_E_ARG,
+                  "the V-tile schedule of the fused conv verify needs a "
+                  "work_counter of 1 + batch * heads = %lld elements",
+                  (long long)(1 + items));
+    if (vt == 0) vt = default_vtiles(items, 8);
+    if (vt <= 1) vt = 2;
+  } else if (schedule == KDA_SCHEDULE_DEFAULT && vt_shape && vt_counter) {
+    // small batches: V-tiles where whole items would leave CUs idle
+    vt = vt != 0 ? vt : default_vtiles(items, 1);
+    if (vt > 1) schedule = KDA_SCHEDULE_V_TILES;
+  }
+  if (schedule == KDA_SCHEDULE_V_TILES && items * vt > 0x7fffffff)
+    return fail(KDA_E_CAPACITY, "batch * heads * v_tiles exceeds 2^31");
+  p.v_tiles = schedule == KDA_SCHEDULE_V_TILES ? vt : 0;
   plan->D = int(D);
   plan->act_bf16 = act == KDA_BF16;
-  plan->noop = a->batch == 0 || T == 0;
+  // No tokens is a no-op, except for the deferred flush: requests with an
+  // empty window still fold their pending positions.
+  plan->noop = a->batch == 0 || (T == 0 && a->pending_lens == nullptr);
   plan->grid = a->max_workgroups;
-  plan->schedule = a->schedule;
+  plan->schedule = schedule;
   return KDA_OK;
 }
 

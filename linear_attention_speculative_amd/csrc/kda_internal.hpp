@@ -43,6 +43,7 @@ struct VerifyParams {
   int32_t n_items;
   int32_t per_ticket;       // items claimed per ticket
   int32_t n_tickets;        // ceil(n_items / per_ticket)
+  int32_t v_tiles;          // V-tile schedule: workgroups per item (2, 4, 8)
 };
 
 constexpr int32_t kOutBf16 = 1;
@@ -123,6 +124,7 @@ struct CompactParams {
 constexpr int kScheduleDefault = 0;
 constexpr int kSchedulePerItem = 1;
 constexpr int kScheduleTickets = 2;
+constexpr int kScheduleVTiles = 3;
 
 // Launchers (return a hipError_t as int).  `grid` <= 0: as many persistent
 // workgroups as are resident at once.

@@ -50,15 +50,27 @@
 namespace kda {
 namespace {
 
-template <int D, int QMAX>
+// DV: state rows (values) one workgroup handles, D for a whole head or a
+// V-tile of D / VT rows.  The per-row arithmetic does not depend on DV (same
+// lanes per row, same column order, same reduction tree), so a V-tiled
+// launch gives the same bits as an untiled one.
+template <int D, int QMAX, int DV = D>
 struct VerifyCfg {
-  static constexpr int NT = D >= 128 ? 256 : (D == 64 ? 128 : 64);
+  static constexpr int NT_HEAD = D >= 128 ? 256 : (D == 64 ? 128 : 64);
   // lanes sharing one state row in the dot-product phase (8 at D = 128:
   // 16 columns per lane, three transposing-reduction steps instead of
   // four; 2% faster at Q = 8, the same at Q = 4)
   static constexpr int L = D >= 128 ? 8 : D >= 64 ? 16 : (D == 32 ? 8 : 4);
+  // A V-tile takes one pass of L lanes per row where it can, but never
+  // fewer threads than columns (the column phase has one thread per
+  // column) or than one wave.
+  static constexpr int NT_MIN = D > 64 ? D : 64;
+  static constexpr int NT =
+      DV == D ? NT_HEAD
+              : (DV * L < NT_MIN ? NT_MIN
+                                 : (DV * L > NT_HEAD ? NT_HEAD : DV * L));
   static constexpr int RPP = NT / L;           // rows per pass
-  static constexpr int PASSES = D / RPP;       // passes over the tile
+  static constexpr int PASSES = DV / RPP;      // passes over the tile
   static constexpr int CHUNKS = D / (4 * L);   // float4 per lane per row
   static constexpr int NVAL = 2 * PASSES;      // row sums per lane, per t
   // Column phase: D >= 64 gives NG groups of D threads (whole waves), each
@@ -75,7 +87,9 @@ struct VerifyCfg {
   static constexpr int NCH = D / CH;
   static constexpr int NB = NV * D <= 5120 ? NV : 5120 / D;
   static constexpr int PART = NB * D > D * DS ? NB * D : D * DS;
-  static constexpr int JC = (3 * D + NT - 1) / NT;  // conv channels/thread
+  // conv channels: q and k of the whole head, v of this workgroup's rows
+  static constexpr int NCONV = 2 * D + DV;
+  static constexpr int JC = (NCONV + NT - 1) / NT;  // conv channels/thread
   static constexpr int JG = (QMAX * D + NT - 1) / NT;  // gate values/thread
   // Register budget: 4 waves per SIMD up to Q = 8 (LDS allows 4
   // workgroups per CU; at Q = 8 this needs the register savings of phases
@@ -84,7 +98,8 @@ struct VerifyCfg {
   // may spill (the build checks it).
   static constexpr int MIN_WAVES = QMAX >= 16 ? 1 : 4;
   static constexpr int TICKET_MIN_WAVES = QMAX >= 16 ? 1 : QMAX >= 8 ? 2 : 3;
-  static_assert(RPP * PASSES == D, "tile rows");
+  static_assert(PASSES >= 1 && RPP * PASSES == DV, "tile rows");
+  static_assert(NT >= D || D < 64, "one thread per column");
   static_assert(CHUNKS * 4 * L == D, "tile columns");
   static_assert(NVAL <= L, "one row sum per lane");
 };
@@ -136,15 +151,19 @@ __device__ __forceinline__ constexpr int idx_n(int t, int s) {
 // Wave-uniform description of one (request, head) work item.
 struct Item {
   int b, h, bos, q, slot, r, a;
+  int v0;        // first state row (value) of a V-tile, else 0
   bool valid, live, rec_ok;
+  bool slot_ok;  // the slot is live, whatever the window length
 };
 
 // The item past the end of a schedule: no view of it holds any byte.
 __device__ __forceinline__ Item no_item() {
   Item it{};
+  it.v0 = 0;
   it.valid = false;
   it.live = false;
   it.rec_ok = false;
+  it.slot_ok = false;
   return it;
 }
 
@@ -154,6 +173,7 @@ __device__ __forceinline__ Item load_item(const VerifyParams& p, int b,
   it.valid = true;
   it.b = b;
   it.h = h;
+  it.v0 = 0;
   int bos, eos, slot, acc;
   sload4(p.qsl + b, p.qsl + b + 1, p.slots + b, p.accepted + b, bos, eos,
          slot, acc);
@@ -162,18 +182,28 @@ __device__ __forceinline__ Item load_item(const VerifyParams& p, int b,
   it.q = (bos < 0 || bos >= p.T) ? 0
                                  : min(min(max(eos - bos, 0), p.Q), p.T - bos);
   it.slot = slot;
-  it.live = it.q > 0 && slot > p.null_id && slot >= 0 && slot < p.N;
+  it.slot_ok = slot > p.null_id && slot >= 0 && slot < p.N;
+  it.live = it.q > 0 && it.slot_ok;
   it.a = min(max(acc, 1), p.Q);
   it.r = p.record_rows ? sload1(p.record_rows + b) : slot;
   it.rec_ok = it.r >= 0 && it.r < p.R;
   return it;
 }
 
-// Per-head constants, raw: conv taps of the head's 3D channels (f32 bits,
+// Conv channel covered by slot j < NCONV of a workgroup: the head's q and k
+// channels first (j < 2D), then the value channels of its rows [v0, v0+DV).
+template <int D, int DV>
+__device__ __forceinline__ void conv_slot(int j, int v0, int& part, int& d) {
+  part = j / D;
+  d = j - part * D;
+  if constexpr (DV != D) d += part == 2 ? v0 : 0;
+}
+
+// Per-head constants, raw: conv taps of the workgroup's channels (f32 bits,
 // or a bf16 in the low half), dt_bias, A_log.
-template <int D, int QMAX>
+template <int D, int QMAX, int DV = D>
 struct HeadRegs {
-  using C = VerifyCfg<D, QMAX>;
+  using C = VerifyCfg<D, QMAX, DV>;
   uint32_t w[C::JC][4];
   float gb[C::JG];
   float alog;
@@ -182,9 +212,9 @@ struct HeadRegs {
 // Raw registers of one item's small loads: conv history, new inputs, gate
 // inputs, beta.  Conversions happen where the values are used, so that no
 // instruction waits for these loads where they are issued.
-template <int D, int QMAX, bool ACT_BF16>
+template <int D, int QMAX, bool ACT_BF16, int DV = D>
 struct Small {
-  using C = VerifyCfg<D, QMAX>;
+  using C = VerifyCfg<D, QMAX, DV>;
   using AT = typename Act<ACT_BF16>::T;
   // dwords of one channel's conv-state row (QMAX + 2 elements)
   static constexpr int RD = (QMAX + 2) * int(sizeof(AT)) / 4;
@@ -196,14 +226,16 @@ struct Small {
 };
 
 // The state tile of one item in registers: lane lg of row group rg holds
-// rows pp * RPP + rg, columns c * 4L + 4 lg .. + 3.
-template <int D, int QMAX>
-using Tile = f4[VerifyCfg<D, QMAX>::PASSES][VerifyCfg<D, QMAX>::CHUNKS];
+// rows v0 + pp * RPP + rg, columns c * 4L + 4 lg .. + 3.
+template <int D, int QMAX, int DV = D>
+using Tile =
+    f4[VerifyCfg<D, QMAX, DV>::PASSES][VerifyCfg<D, QMAX, DV>::CHUNKS];
 
-template <int D, int QMAX>
+template <int D, int QMAX, int DV = D>
 __device__ __forceinline__ void load_head(const VerifyParams& p, int h,
-                                          HeadRegs<D, QMAX>& hr) {
-  using C = VerifyCfg<D, QMAX>;
+                                          HeadRegs<D, QMAX, DV>& hr,
+                                          int v0 = 0) {
+  using C = VerifyCfg<D, QMAX, DV>;
   const int tid = fresh_tid();
   const int HD = p.H * D;
   const bool w_bf16 = (p.flags & kWBf16) != 0;
@@ -213,8 +245,9 @@ __device__ __forceinline__ void load_head(const VerifyParams& p, int h,
 #pragma unroll
     for (int i = 0; i < 4; ++i) hr.w[jj][i] = 0;
     const int j = tid + jj * C::NT;
-    if (conv && j < 3 * D) {
-      const int part = j / D, d = j - part * D;
+    if (conv && j < C::NCONV) {
+      int part, d;
+      conv_slot<D, DV>(j, v0, part, d);
       const uint32_t ch = part * HD + h * D + d;
       if (p.flags & kWRow) {
         // the channel's taps in one load; bf16 taps stay packed two per
@@ -275,20 +308,112 @@ __device__ __forceinline__ uint32_t bits_of(AT v) {
     return __float_as_uint(v);
 }
 
-// Phase 0 of a live item: conv + SiLU of the head's 3D channels, key
-// record, conv roll; `mid()` runs between the conv and the gate (the
-// one-workgroup-per-item kernel issues the second half of its tile there);
-// gate decays, raw-gate record half, sigmoid(beta).
+// The three history entries (positions a-1 .. a+1 of the conv state) of
+// conv slot jj, as loaded.
+template <int D, int QMAX, bool ACT_BF16, int DV>
+__device__ __forceinline__ void history3(
+    const VerifyParams& p, const Item& it,
+    const Small<D, QMAX, ACT_BF16, DV>& s, int jj,
+    typename Act<ACT_BF16>::T (&hv)[3]) {
+  using AT = typename Act<ACT_BF16>::T;
+  hv[0] = s.hist[jj][0];
+  hv[1] = s.hist[jj][1];
+  hv[2] = s.hist[jj][2];
+  if (p.flags & kConvRow) {
+    hv[0] = row_at<AT, 0, QMAX>(s.row[jj], it.a - 1);
+    hv[1] = row_at<AT, 1, QMAX>(s.row[jj], it.a - 1);
+    hv[2] = row_at<AT, 2, QMAX>(s.row[jj], it.a - 1);
+  }
+}
+
+// Roll of conv channel `ch` (conv slot jj) in place: the two newest history
+// entries, then the q new inputs, at the front; positions past 2 + q keep
+// their bytes.  h1, h2: history entries a and a+1.
+template <int D, int QMAX, bool ACT_BF16, bool FULL, int DV>
+__device__ __forceinline__ void roll_channel(
+    const VerifyParams& p, const Item& it,
+    const Small<D, QMAX, ACT_BF16, DV>& s, int jj, int ch,
+    typename Act<ACT_BF16>::T h1, typename Act<ACT_BF16>::T h2) {
+  using AT = typename Act<ACT_BF16>::T;
+  using S = Small<D, QMAX, ACT_BF16, DV>;
+  const int q = FULL ? QMAX : it.q;
+  AT* __restrict__ cs =
+      static_cast<AT*>(p.conv_state) + int64_t(it.slot) * p.s_cs_slot;
+  AT* csc = cs + ch * p.s_cs_chan;
+  if (p.flags & kConvRow) {
+    // the whole row in one pass; its tail is written back unchanged
+    constexpr int RE = QMAX + 2;
+    constexpr int EW = 4 / int(sizeof(AT));  // elements per dword
+    uint32_t nw[S::RD];
+#pragma unroll
+    for (int i = 0; i < S::RD; ++i) nw[i] = 0;
+    [&]<int... E>(std::integer_sequence<int, E...>) {
+      auto put = [&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        AT v;
+        if constexpr (e == 0)
+          v = h1;
+        else if constexpr (e == 1)
+          v = h2;
+        else
+          v = (e - 2 < q) ? s.xs[jj][e - 2] : row_elem<AT, e>(s.row[jj]);
+        nw[e / EW] |= bits_of(v) << (32 / EW * (e % EW));
+      };
+      (put(std::integral_constant<int, E>{}), ...);
+    }(std::make_integer_sequence<int, RE>{});
+    uint32_t* wp = reinterpret_cast<uint32_t*>(csc);
+#pragma unroll
+    for (int i = 0; i < S::RD; ++i) wp[i] = nw[i];
+  } else {
+    const int s_ct = p.s_cs_tok;
+    csc[0] = h1;
+    csc[s_ct] = h2;
+#pragma unroll
+    for (int t = 0; t < QMAX; ++t)
+      if (t < q) csc[(2 + t) * s_ct] = s.xs[jj][t];
+  }
+}
+
+// The deferred roll of the head's q and k channels (conv slots j < 2D) by
+// the last V-tile of an item to have read their history.
+template <int D, int QMAX, bool ACT_BF16, bool FULL, int DV>
+__device__ __forceinline__ void roll_qk(const VerifyParams& p, const Item& it,
+                                        const Small<D, QMAX, ACT_BF16, DV>& s) {
+  using C = VerifyCfg<D, QMAX, DV>;
+  using AT = typename Act<ACT_BF16>::T;
+  const int tid = fresh_tid();
+  const int HD = p.H * D;
+#pragma unroll
+  for (int jj = 0; jj < C::JC; ++jj) {
+    const int j = tid + jj * C::NT;
+    if (j < 2 * D) {
+      const int part = j / D, d = j - part * D;
+      AT hv[3];
+      history3<D, QMAX, ACT_BF16, DV>(p, it, s, jj, hv);
+      roll_channel<D, QMAX, ACT_BF16, FULL, DV>(p, it, s, jj,
+                                                part * HD + it.h * D + d,
+                                                hv[1], hv[2]);
+    }
+  }
+}
+
+// Phase 0 of a live item: conv + SiLU of the workgroup's channels (the
+// head's 3D, or q, k and a V-tile's values), key record, conv roll;
+// `mid()` runs between the conv and the gate (the one-workgroup-per-item
+// kernel issues the second half of its tile there); gate decays, raw-gate
+// record half, sigmoid(beta).
 // FULL: the request verifies all QMAX positions (q == QMAX), so every
-// position guard folds away at compile time.
-template <int D, int QMAX, bool ACT_BF16, bool FULL, class Mid>
-__device__ __forceinline__ void item_front(const VerifyParams& p,
-                                           VerifySmem<D, QMAX>& sm,
-                                           const Item& it,
-                                           const Small<D, QMAX, ACT_BF16>& s,
-                                           const HeadRegs<D, QMAX>& hr,
-                                           Mid&& mid) {
-  using C = VerifyCfg<D, QMAX>;
+// position guard folds away at compile time.  ROLL_QK false (V-tiles): the
+// q and k channels, whose history every V-tile of the item reads, are not
+// rolled here (roll_qk does it once all have read it), and each V-tile
+// writes only its own columns of the key/gate record.
+template <int D, int QMAX, bool ACT_BF16, bool FULL, int DV = D,
+          bool ROLL_QK = true, class Mid>
+__device__ __forceinline__ void item_front(
+    const VerifyParams& p, VerifySmem<D, QMAX>& sm, const Item& it,
+    const Small<D, QMAX, ACT_BF16, DV>& s, const HeadRegs<D, QMAX, DV>& hr,
+    Mid&& mid) {
+  using C = VerifyCfg<D, QMAX, DV>;
   using A = Act<ACT_BF16>;
   using AT = typename A::T;
   const int tid = fresh_tid();
@@ -296,24 +421,24 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
   const int q = FULL ? QMAX : it.q;
   const bool rec_ok = it.rec_ok;
   const int HD = p.H * D;
-  AT* __restrict__ cs =
-      static_cast<AT*>(p.conv_state) + int64_t(it.slot) * p.s_cs_slot;
+  const int v0 = DV == D ? 0 : it.v0;
   const int64_t kg_off =
       int64_t(it.r) * p.s_kg_row + int64_t(h) * p.s_kg_head;
   float* __restrict__ kg32 = static_cast<float*>(p.key_gate) + kg_off;
   uint16_t* __restrict__ kg16 = static_cast<uint16_t*>(p.key_gate) + kg_off;
-  const int s_cc = p.s_cs_chan, s_ct = p.s_cs_tok;
   const int s_kp = p.s_kg_pos;
   const bool kg_bf16 = (p.flags & kKgBf16) != 0;
   const bool w_bf16 = (p.flags & kWBf16) != 0;
-  const bool row_fast = (p.flags & kConvRow) != 0;
   const bool conv = (p.flags & kNoConv) == 0;
+  // the columns of the key/gate record this workgroup writes
+  auto own_col = [&](int d) { return DV == D || (d >= v0 && d < v0 + DV); };
 
 #pragma unroll
   for (int jj = 0; jj < C::JC; ++jj) {
     const int j = tid + jj * C::NT;
-    if (j < 3 * D) {
-      const int part = j / D, d = j - part * D;
+    if (j < C::NCONV) {
+      int part, d;
+      conv_slot<D, DV>(j, v0, part, d);
       const int ch = part * HD + h * D + d;
       float w[4];
       if (w_bf16 && (p.flags & kWRow)) {
@@ -328,13 +453,9 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
           w[i] = __uint_as_float(w_bf16 ? hr.w[jj][i] << 16 : hr.w[jj][i]);
       }
       // history: positions a-1 .. a+1 of the conv state
-      AT h0 = s.hist[jj][0], h1 = s.hist[jj][1], h2 = s.hist[jj][2];
-      if (row_fast) {
-        h0 = row_at<AT, 0, QMAX>(s.row[jj], it.a - 1);
-        h1 = row_at<AT, 1, QMAX>(s.row[jj], it.a - 1);
-        h2 = row_at<AT, 2, QMAX>(s.row[jj], it.a - 1);
-      }
-      float s0 = A::f(h0), s1 = A::f(h1), s2 = A::f(h2);
+      AT hv[3];
+      history3<D, QMAX, ACT_BF16, DV>(p, it, s, jj, hv);
+      float s0 = A::f(hv[0]), s1 = A::f(hv[1]), s2 = A::f(hv[2]);
 #pragma unroll
       for (int t = 0; t < QMAX; ++t) {
         if (t < q) {
@@ -346,7 +467,7 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
           // (the unfused entry receives the convolved value itself)
           const float yv = conv ? acc * sigmoidf_(acc) : s3;
           sm.y[part][t][d] = yv;
-          if (part == 1 && rec_ok) {
+          if (part == 1 && rec_ok && own_col(d)) {
             if (kg_bf16)
               kg16[t * s_kp + d] = f32_to_bf16(yv);
             else
@@ -357,43 +478,9 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
           s2 = s3;
         }
       }
-      // Roll: the two newest history entries, then the q new inputs, at
-      // the front; positions past 2 + q keep their bytes.
-      AT* csc = cs + ch * s_cc;
-      if (!conv) {
-        // no conv state
-      } else if (row_fast) {
-        // the whole row in one pass; its tail is written back unchanged
-        constexpr int RE = QMAX + 2;
-        constexpr int EW = 4 / int(sizeof(AT));  // elements per dword
-        uint32_t nw[Small<D, QMAX, ACT_BF16>::RD];
-#pragma unroll
-        for (int i = 0; i < Small<D, QMAX, ACT_BF16>::RD; ++i) nw[i] = 0;
-        [&]<int... E>(std::integer_sequence<int, E...>) {
-          auto put = [&](auto ec) {
-            constexpr int e = decltype(ec)::value;
-            AT v;
-            if constexpr (e == 0)
-              v = h1;
-            else if constexpr (e == 1)
-              v = h2;
-            else
-              v = (e - 2 < q) ? s.xs[jj][e - 2]
-                              : row_elem<AT, e>(s.row[jj]);
-            nw[e / EW] |= bits_of(v) << (32 / EW * (e % EW));
-          };
-          (put(std::integral_constant<int, E>{}), ...);
-        }(std::make_integer_sequence<int, RE>{});
-        uint32_t* wp = reinterpret_cast<uint32_t*>(csc);
-#pragma unroll
-        for (int i = 0; i < Small<D, QMAX, ACT_BF16>::RD; ++i) wp[i] = nw[i];
-      } else {
-        csc[0] = h1;
-        csc[s_ct] = h2;
-#pragma unroll
-        for (int t = 0; t < QMAX; ++t)
-          if (t < q) csc[(2 + t) * s_ct] = s.xs[jj][t];
-      }
+      if (conv && (ROLL_QK || part == 2))
+        roll_channel<D, QMAX, ACT_BF16, FULL, DV>(p, it, s, jj, ch, hv[1],
+                                                  hv[2]);
     }
   }
 
@@ -408,7 +495,7 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
     if (t < q) {
       const float g0 = A::f(s.gv[jj]);
       sm.dec[t][k] = __expf(kda_gate(g0 + hr.gb[jj], Ah, use_lb, p.lb));
-      if (rec_ok) {
+      if (rec_ok && own_col(k)) {
         if (kg_bf16)
           kg16[t * s_kp + D + k] = f32_to_bf16(g0);
         else
@@ -420,13 +507,14 @@ __device__ __forceinline__ void item_front(const VerifyParams& p,
 }
 
 // Phases 1-4 of a live item (after the barrier that publishes phase 0),
-// with its state tile in registers.
-template <int D, int QMAX, bool FULL, class PreDots>
+// with its state tile (rows v0 .. v0 + DV) in registers.
+template <int D, int QMAX, bool FULL, int DV = D, class PreDots>
 __device__ __forceinline__ void item_back(const VerifyParams& p,
                                           VerifySmem<D, QMAX>& sm,
-                                          const Item& it, Tile<D, QMAX>& st,
+                                          const Item& it,
+                                          Tile<D, QMAX, DV>& st,
                                           PreDots&& pre_dots) {
-  using C = VerifyCfg<D, QMAX>;
+  using C = VerifyCfg<D, QMAX, DV>;
   const int tid = fresh_tid();
   const int h = it.h;
   const int q = FULL ? QMAX : it.q;
@@ -577,8 +665,8 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
   lds_barrier();
 
   // ---- phase 4: per-row triangular solve, outputs and corrections -------------
-  if (tid < D) {
-    const int v = tid;
+  if (tid < DV) {
+    const int v = (DV == D ? 0 : it.v0) + tid;   // state row (value)
     // wave-uniform bases, 32-bit per-lane offsets
     float* __restrict__ corr = p.correction + int64_t(it.r) * p.s_c_row +
                                int64_t(h) * p.s_c_head;
@@ -586,7 +674,7 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
     float* __restrict__ out32 = static_cast<float*>(p.out) + ob;
     uint16_t* __restrict__ out16 = static_cast<uint16_t*>(p.out) + ob;
     const int s_cp = p.s_c_pos, s_out = p.s_out;
-    const float* drow = &sm.part[v * C::DS];
+    const float* drow = &sm.part[tid * C::DS];
     float cc[QMAX];
 #pragma unroll
     for (int t = 0; t < QMAX; ++t) {
@@ -744,6 +832,36 @@ __device__ __forceinline__ void flush_fold(const VerifyParams& p,
   }
 }
 
+// The deferred flush of an item whose slot is live but whose window is
+// empty (q = 0): the pending positions are still folded into the checkpoint
+// and written back; nothing else is read or written.
+template <int D, int QMAX>
+__device__ __forceinline__ void flush_only_item(const VerifyParams& p,
+                                                FlushSmem<D, QMAX, true>& fs,
+                                                const Item& it) {
+  using C = VerifyCfg<D, QMAX>;
+  if (!it.rec_ok) return;
+  const int n = min(max(sload1(p.pending + it.b), 0), p.Q);
+  if (n == 0) return;
+  const int tid = fresh_tid();
+  HeadRegs<D, QMAX> hr;
+  load_head<D, QMAX>(p, it.h, hr);
+  PendingRegs<D, QMAX> pr;
+  load_pending<D, QMAX>(p, it, n, pr);
+  const int lg = tid % C::L, rg = tid / C::L;
+  const float* __restrict__ sbase =
+      p.state + int64_t(it.slot) * p.s_slot + int64_t(it.h) * D * D;
+  Tile<D, QMAX> st;
+#pragma unroll
+  for (int pp = 0; pp < C::PASSES; ++pp)
+#pragma unroll
+    for (int c = 0; c < C::CHUNKS; ++c)
+      st[pp][c] = ld_stream(sbase + (pp * C::RPP + rg) * D + c * 4 * C::L +
+                            4 * lg);
+  flush_prepare<D, QMAX>(p, fs, n, pr, hr);
+  flush_fold<D, QMAX>(p, fs, it, n, st);
+}
+
 // Null block (null or out-of-pool slot): +0.0 outputs, no state, record or
 // conv byte touched.
 template <int D, int QMAX>
@@ -761,22 +879,28 @@ __device__ __forceinline__ void null_item(const VerifyParams& p,
 // schedules).  `drawn` is thread 0's freshly drawn ticket; it is published
 // through LDS at the first barrier, after which `advance()` starts the
 // scalar loads of the next item's metadata.
+// DV < D: one V-tile of the item (rows it.v0 .. it.v0 + DV); `advance()`
+// then performs its arrival (see kda_verify_vtile_kernel) and LDS
+// ticket[1] says, from the next barrier on, whether this V-tile rolls the
+// q and k channels.
 template <int D, int QMAX, bool ACT_BF16, bool FULL, bool FLUSH,
-          bool PERSISTENT, class Advance>
+          bool PERSISTENT, int DV = D, class Advance>
 __device__ __forceinline__ void verify_item(const VerifyParams& p,
                                             VerifySmem<D, QMAX>& sm,
                                             FlushSmem<D, QMAX, FLUSH>& fs,
                                             const Item& it, int drawn,
                                             int buf, Advance&& advance) {
-  using C = VerifyCfg<D, QMAX>;
+  using C = VerifyCfg<D, QMAX, DV>;
   using AT = typename Act<ACT_BF16>::T;
+  static_assert(DV == D || !(FLUSH || PERSISTENT), "V-tiles: plain verify");
   const int tid = threadIdx.x;
   const int h = it.h;
   const int q = FULL ? QMAX : it.q;
   const int HD = p.H * D;
+  const int v0 = DV == D ? 0 : it.v0;
   // small loads first (vector-memory counters retire in issue order)
-  HeadRegs<D, QMAX> hr;
-  load_head<D, QMAX>(p, h, hr);
+  HeadRegs<D, QMAX, DV> hr;
+  load_head<D, QMAX, DV>(p, h, hr, v0);
   // deferred flush: positions still pending in the record row
   int n_pend = 0;
   PendingRegs<D, QMAX> pr;
@@ -784,7 +908,7 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
     if (it.rec_ok) n_pend = min(max(sload1(p.pending + it.b), 0), p.Q);
     if (n_pend > 0) load_pending<D, QMAX>(p, it, n_pend, pr);
   }
-  Small<D, QMAX, ACT_BF16> s;
+  Small<D, QMAX, ACT_BF16, DV> s;
   {
     const AT* __restrict__ xq =
         static_cast<const AT*>(p.mixed_qkv) + int64_t(it.bos) * p.s_x;
@@ -798,8 +922,9 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
 #pragma unroll
     for (int jj = 0; jj < C::JC; ++jj) {
       const int j = tid + jj * C::NT;
-      if (j < 3 * D) {
-        const int part = j / D, d = j - part * D;
+      if (j < C::NCONV) {
+        int part, d;
+        conv_slot<D, DV>(j, v0, part, d);
         const int ch = part * HD + h * D + d;
         if (p.flags & kNoConv) {
           // q | k | v given after the convolution: no history
@@ -808,7 +933,7 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
         } else if (p.flags & kConvRow) {
           const uint32_t* rp = reinterpret_cast<const uint32_t*>(cs + ch * s_cc);
 #pragma unroll
-          for (int i = 0; i < Small<D, QMAX, ACT_BF16>::RD; ++i)
+          for (int i = 0; i < Small<D, QMAX, ACT_BF16, DV>::RD; ++i)
             s.row[jj][i] = rp[i];
         } else {
           const int co = ch * s_cc + (it.a - 1) * s_ct;
@@ -842,10 +967,10 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
   // the state tile, in two halves (the second once the conv registers are
   // free)
   const int lg = tid % C::L, rg = tid / C::L;
-  const float* __restrict__ sbase =
-      p.state + int64_t(it.slot) * p.s_slot + int64_t(h) * D * D;
+  const float* __restrict__ sbase = p.state + int64_t(it.slot) * p.s_slot +
+                                   int64_t(h) * D * D + v0 * D;
   constexpr int P0 = (C::PASSES + 1) / 2;
-  Tile<D, QMAX> st;
+  Tile<D, QMAX, DV> st;
 #pragma unroll
   for (int pp = 0; pp < P0; ++pp)
 #pragma unroll
@@ -857,7 +982,7 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
   if constexpr (FLUSH) {
     if (n_pend > 0) flush_prepare<D, QMAX>(p, fs, n_pend, pr, hr);
   }
-  item_front<D, QMAX, ACT_BF16, FULL>(p, sm, it, s, hr, [&] {
+  item_front<D, QMAX, ACT_BF16, FULL, DV, DV == D>(p, sm, it, s, hr, [&] {
 #pragma unroll
     for (int pp = P0; pp < C::PASSES; ++pp)
 #pragma unroll
@@ -869,9 +994,14 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
   lds_barrier();
   // Metadata of the next item: scalar loads in flight from here on.
   advance();
-  item_back<D, QMAX, FULL>(p, sm, it, st, [&](Tile<D, QMAX>& t) {
+  item_back<D, QMAX, FULL, DV>(p, sm, it, st, [&](Tile<D, QMAX, DV>& t) {
     if constexpr (FLUSH) {
       if (n_pend > 0) flush_fold<D, QMAX>(p, fs, it, n_pend, t);
+    }
+    if constexpr (DV != D) {
+      // the last V-tile to arrive rolls the q and k channels
+      if ((p.flags & kNoConv) == 0 && sm.ticket[1] != 0)
+        roll_qk<D, QMAX, ACT_BF16, FULL, DV>(p, it, s);
     }
   });
 }
@@ -970,10 +1100,76 @@ __global__ void __launch_bounds__((VerifyCfg<D, QMAX>::NT),
     else
       verify_item<D, QMAX, ACT_BF16, false, FLUSH, false>(p, sm, fs, it, 0, 0,
                                                    advance);
+  } else if (FLUSH && it.slot_ok) {
+    // live slot, empty window: only the deferred flush
+    if constexpr (FLUSH) flush_only_item<D, QMAX>(p, fs, it);
   } else {
     // Null block: zero outputs, touch no state, record or conv byte.
     for (int j = threadIdx.x; j < it.q * D; j += C::NT) {
       const int t = j / D, v = j - t * D;
+      st_elem(p.out, int64_t(it.bos + t) * p.s_out + int64_t(it.h) * D + v,
+              0.0f, (p.flags & kOutBf16) != 0);
+    }
+  }
+}
+
+// One workgroup per (request, head, V-tile): each of the VT = D / DV
+// workgroups of a (request, head) item verifies DV rows of its state (the
+// ops page launches its verify on a (V-blocks, requests, heads) grid), for
+// batches too small to fill the GPU with whole items.  Every V-tile computes
+// the conv of the head's q and k channels (all of them feed its column
+// phase) and of its own value channels, which it also rolls.  The q and k
+// channels are rolled once, by the last V-tile of the item to have read
+// their history: after the barrier that follows phase 0 (every thread of
+// the workgroup has used its loaded history by then), thread 0 adds 1 to
+// the item's arrival counter work_counter[1 + b * H + h]; the V-tile that
+// sees VT - 1 sets it back to 0 and rolls them.  Results are bitwise those
+// of kda_verify_grid_kernel.
+template <int D, int QMAX, bool ACT_BF16, int DV>
+__global__ void __launch_bounds__((VerifyCfg<D, QMAX, DV>::NT),
+                                  (VerifyCfg<D, QMAX, DV>::MIN_WAVES))
+    kda_verify_vtile_kernel(VerifyParams p) {
+  using C = VerifyCfg<D, QMAX, DV>;
+  constexpr int VT = D / DV;
+  __shared__ VerifySmem<D, QMAX> sm;
+  FlushSmem<D, QMAX, false> nofs;
+  // XCD-aware order over (request, head, V-tile) with the V-tile fastest,
+  // so that the V-tiles of one item share an XCD's L2 (they all read the
+  // item's q and k inputs)
+  const int n = p.B * p.H * VT;
+  const int lin = int(blockIdx.x);
+  const int item = (n & 7) == 0 ? (lin & 7) * (n >> 3) + (lin >> 3) : lin;
+  const int bh = item / VT;
+  const int ib = bh / p.H;
+  Item it = load_item(p, uniform(ib), uniform(bh - ib * p.H));
+  it.v0 = uniform(item - bh * VT) * DV;
+  int* __restrict__ arrive = p.counter + 1 + bh;
+  // Arrival (right after the phase-0 barrier).  The increment is read back
+  // from LDS, where thread 0 stored it before the barrier, so the atomic
+  // cannot be issued before every wave has passed that barrier.
+  auto advance = [&] {
+    if (threadIdx.x == 0 && (p.flags & kNoConv) == 0) {
+      const int inc = sm.ticket[0];
+      const int old = atomicAdd(arrive, inc);
+      const int last = old == VT - 1 ? 1 : 0;
+      if (last)
+        __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      sm.ticket[1] = last;
+    }
+  };
+  if (it.live) {
+    // drawn = 1 with buf = 1: thread 0 stores the increment 1 in ticket[0]
+    if (it.q == QMAX)
+      verify_item<D, QMAX, ACT_BF16, true, false, false, DV>(p, sm, nofs, it,
+                                                             1, 1, advance);
+    else
+      verify_item<D, QMAX, ACT_BF16, false, false, false, DV>(p, sm, nofs, it,
+                                                              1, 1, advance);
+  } else {
+    // Null block: zero this V-tile's outputs, touch nothing else.
+    for (int j = threadIdx.x; j < it.q * DV; j += C::NT) {
+      const int t = j / DV, v = it.v0 + (j - t * DV);
       st_elem(p.out, int64_t(it.bos + t) * p.s_out + int64_t(it.h) * D + v,
               0.0f, (p.flags & kOutBf16) != 0);
     }
@@ -1002,6 +1198,36 @@ int resident_grid(K kern, int threads, int* cache, int* out) {
   return 0;
 }
 
+// V-tiles of a head with D rows: VT = 2, 4 or 8 (head dims 64 and 128,
+// windows up to 8).
+template <int D, int QMAX, bool ACT_BF16>
+int launch_vtiles(const VerifyParams& p, int vt, hipStream_t stream) {
+  if constexpr ((D == 64 || D == 128) && QMAX <= 8) {
+    const int64_t n = int64_t(p.B) * p.H * vt;
+    if (n > 0x7fffffff) return int(hipErrorInvalidConfiguration);
+    switch (vt) {
+      case 2:
+        hipLaunchKernelGGL((kda_verify_vtile_kernel<D, QMAX, ACT_BF16, D / 2>),
+                           dim3(unsigned(n)),
+                           dim3(VerifyCfg<D, QMAX, D / 2>::NT), 0, stream, p);
+        return int(hipGetLastError());
+      case 4:
+        hipLaunchKernelGGL((kda_verify_vtile_kernel<D, QMAX, ACT_BF16, D / 4>),
+                           dim3(unsigned(n)),
+                           dim3(VerifyCfg<D, QMAX, D / 4>::NT), 0, stream, p);
+        return int(hipGetLastError());
+      case 8:
+        hipLaunchKernelGGL((kda_verify_vtile_kernel<D, QMAX, ACT_BF16, D / 8>),
+                           dim3(unsigned(n)),
+                           dim3(VerifyCfg<D, QMAX, D / 8>::NT), 0, stream, p);
+        return int(hipGetLastError());
+      default:
+        return int(hipErrorInvalidValue);
+    }
+  }
+  return int(hipErrorInvalidValue);
+}
+
 template <int D, int QMAX, bool ACT_BF16>
 int launch_one(const VerifyParams& p, int schedule, int grid,
                hipStream_t stream) {
@@ -1015,6 +1241,8 @@ int launch_one(const VerifyParams& p, int schedule, int grid,
                        dim3(p.H, p.B), dim3(C::NT), 0, stream, p);
     return int(hipGetLastError());
   }
+  if (schedule == kScheduleVTiles && p.v_tiles > 1)
+    return launch_vtiles<D, QMAX, ACT_BF16>(p, p.v_tiles, stream);
   if (schedule != kScheduleTickets && p.B <= 65535) {
     hipLaunchKernelGGL((kda_verify_grid_kernel<D, QMAX, ACT_BF16, false>),
                        dim3(p.H, p.B), dim3(C::NT), 0, stream, p);

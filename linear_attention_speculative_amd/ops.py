@@ -84,7 +84,8 @@ def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
                 num_accepted_tokens, spec_query_len, conv_dim_first,
                 work_counter, record_rows=None, null_block_id=0,
                 max_workgroups=0, items_per_ticket=0,
-                schedule=0, pending_lens=None) -> _abi.KdaVerifyArgs:
+                schedule=0, pending_lens=None,
+                v_tiles=0) -> _abi.KdaVerifyArgs:
     a = _abi.KdaVerifyArgs()
     a.mixed_qkv = describe(mixed_qkv)
     a.raw_gate = describe(raw_gate)
@@ -112,6 +113,8 @@ def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
     a.items_per_ticket = items_per_ticket
     a.schedule = schedule
     a.pending_lens = _ptr(pending_lens)
+    a.work_counter_len = 0 if work_counter is None else work_counter.numel()
+    a.v_tiles = v_tiles
     return a
 
 

@@ -49,11 +49,18 @@ def run_oracle_verify_qkv(sample: Sample) -> dict:
 
 
 def check_verify(wl, layer: int, sample: Sample, ref: dict,
-                 kg_k_tol: float = None) -> dict:
+                 kg_k_tol: float = None, rec_before=None,
+                 extra_tol: float = 0.0) -> dict:
     """Compare the GPU tensors of `layer` (after the verify launch) with the
-    oracle results `ref` for the sample.  Returns the measured errors."""
+    oracle results `ref` for the sample.  Returns the measured errors.
+
+    Record positions the launch does not write must keep their bytes: by
+    default the oracle's inputs hold them; `rec_before` = (correction,
+    key_gate) GPU tensors cloned before the launch is used instead when an
+    earlier launch wrote them.  `extra_tol` widens every float bound (one
+    bf16 step when the key record is stored in the activation dtype)."""
     L = wl.layers[layer]
-    tol = TOL[wl.act]
+    tol = TOL[wl.act] + extra_tol
     errs = {}
     dev = L.state.device
     tok_all = [t for ts in sample.tok for t in ts]
@@ -103,19 +110,24 @@ def check_verify(wl, layer: int, sample: Sample, ref: dict,
         nr = [n for _, _, n in rec]
         corr_ref = ref["correction"][nr]
         kg_ref = ref["key_gate"][nr]
+        if rec_before is not None:
+            kept_c = f64(rec_before[0].index_select(0, ridx))
+            kept_k = f64(rec_before[1].index_select(0, ridx))
+        else:
+            kept_c, kept_k = corr_ref, kg_ref
         w = ref["rec_written"][nr]                      # [n, H, Q]
         wc = np.broadcast_to(w[..., None], corr_ref.shape)
         errs["correction"] = rel_err(corr_gpu[wc], corr_ref[wc])
         assert errs["correction"] <= tol, ("correction", errs["correction"])
-        # unwritten positions keep their bytes (ref holds the inputs there)
-        assert np.array_equal(corr_gpu[~wc], corr_ref[~wc])
+        # unwritten positions keep their bytes
+        assert np.array_equal(corr_gpu[~wc], kept_c[~wc])
         wk = np.broadcast_to(w[..., None], kg_ref[..., :D].shape)
         kt = kg_k_tol if kg_k_tol is not None else tol
         errs["key"] = rel_err(kg_gpu[..., :D][wk], kg_ref[..., :D][wk])
         assert errs["key"] <= kt, ("key record", errs["key"])
-        assert np.array_equal(kg_gpu[..., D:], kg_ref[..., D:]), \
+        assert np.array_equal(kg_gpu[..., D:][wk], kg_ref[..., D:][wk]), \
             "raw gate record half must be an exact copy"
-        assert np.array_equal(kg_gpu[..., :D][~wk], kg_ref[..., :D][~wk])
+        assert np.array_equal(kg_gpu[~w], kept_k[~w])
     return errs
 
 
@@ -130,9 +142,13 @@ def commit_layer_inputs(sample: Sample, ref: dict, L) -> dict:
 
 
 def check_commit(wl, layer: int, sample: Sample, new_state: np.ndarray,
-                 written: np.ndarray, final_slots=None) -> float:
+                 written: np.ndarray, final_slots=None,
+                 extra_tol: float = 0.0) -> float:
     """Compare the GPU checkpoint of `layer` after the commit with the
-    oracle's committed states of the sample (compact pool)."""
+    oracle's committed states of the sample (compact pool).  `extra_tol`
+    widens the bound (one bf16 step for a key record stored in the
+    activation dtype: the two sides may round a key element to neighbouring
+    bf16 values)."""
     L = wl.layers[layer]
     dev = L.state.device
     idx, cidx = [], []
@@ -147,5 +163,37 @@ def check_commit(wl, layer: int, sample: Sample, new_state: np.ndarray,
         return 0.0
     gpu = f64(L.state.index_select(0, torch.tensor(idx, device=dev)))
     err = rel_err(gpu, new_state[cidx])
-    assert err <= TOL[wl.act], ("committed state", err)
+    assert err <= TOL[wl.act] + extra_tol, ("committed state", err)
     return err
+
+
+def kg_extra_tol(wl) -> float:
+    """Widening of the float bounds downstream of an activation-dtype key
+    record: GPU (fp32 k, then RNE) and oracle (fp64 k, then RNE) may round a
+    key element to neighbouring bf16 values, one bf16 step (2^-8 of the
+    element) apart."""
+    return 2.0 ** -8 if wl.kg_dtype == "bf16" else 0.0
+
+
+def full_inputs(wl, layer: int) -> dict:
+    """Oracle keyword arguments for every request of `layer` over the whole
+    (uncompacted) pool, copied from the seeded tensors as they are now: take
+    it before any launch writes them, so that no value the HIP path produced
+    becomes an oracle input."""
+    L = wl.layers[layer]
+    return dict(
+        mixed_qkv=f64(L.mixed_qkv), raw_gate=f64(L.raw_gate),
+        raw_beta=f64(L.raw_beta), A_log=f64(L.A_log), dt_bias=f64(L.dt_bias),
+        state=f64(L.state), correction=f64(L.correction),
+        key_gate=f64(L.key_gate), out=np.zeros((wl.T, wl.H * wl.D)),
+        conv_state=f64(wl.conv_state_dim_first(layer)),
+        conv_weight=f64(L.conv_weight),
+        query_start_loc=wl.query_start_loc.cpu().numpy().astype(np.int64),
+        state_indices=wl.state_indices.cpu().numpy().astype(np.int64),
+        num_accepted_tokens=wl.num_accepted_tokens.cpu().numpy()
+        .astype(np.int64),
+        spec_query_len=wl.Q, null_block_id=wl.null_block_id,
+        use_lower_bound=L.use_lower_bound, lower_bound=L.lower_bound,
+        record_rows=None if wl.record_rows is None
+        else wl.record_rows.cpu().numpy().astype(np.int64),
+        key_gate_dtype=wl.kg_dtype)

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_abi.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert kda.abi_version() == 4
+    assert kda.abi_version() == 5
     assert lib.kda_status_string(_abi.KDA_E_UNALIGNED) == b"KDA_E_UNALIGNED"
 
 
@@ -161,7 +161,7 @@ def test_capacity_and_argument_errors():
         assert _code(kw) == 0
     kw["schedule"] = _abi.KDA_SCHEDULE_TICKETS
     assert _code(kw) == _abi.KDA_E_ARG
-    for bad in (-1, 3):
+    for bad in (-1, 4):
         kw["schedule"] = bad
         assert _code(kw) == _abi.KDA_E_ARG
     kw["schedule"] = 0
@@ -438,3 +438,56 @@ def test_commit_step_checks():
     assert code(ca, pa, xa) == _abi.KDA_E_ARG
     assert lib.kda_check_commit_step(None, ctypes.byref(pa), None) == \
         _abi.KDA_E_ARG
+
+
+def test_byte_offsets_of_strided_outputs_fit_32_bits():
+    # An fp32 `out` whose row stride keeps the element offsets of a window
+    # under 2^31 but its byte offsets over it is refused (the kernel forms
+    # those byte offsets in 32 bits).  Descriptors are edited directly: no
+    # tensor of that extent is allocated.
+    from linear_attention_speculative_amd.ops import verify_args
+    wl, kw = _kw()
+    a = verify_args(**kw)
+    lib = _abi.load()
+    assert lib.kda_check_verify(ctypes.byref(a)) == 0
+    a.out.stride[0] = 1 << 28          # Q * stride = 2^30 elements, 2^32 B
+    assert lib.kda_check_verify(ctypes.byref(a)) == _abi.KDA_E_LAYOUT
+    assert b"byte offsets" in lib.kda_last_error()
+    a = verify_args(**kw)
+    a.correction.stride[2] = 1 << 28   # correction positions, fp32
+    assert lib.kda_check_verify(ctypes.byref(a)) == _abi.KDA_E_LAYOUT
+
+
+def test_vtile_schedule_checks():
+    # explicit V-tiles: head dims 64 and 128, windows up to 8, no pending
+    # records, and a counter with one arrival slot per (request, head)
+    wl = make_workload("ragged", B=4, H=2, D=64, Q=4, N=8)
+    big = torch.zeros(1 + wl.B * wl.H, dtype=torch.int32)
+    kw = verify_kwargs(wl, 0, big, schedule=_abi.KDA_SCHEDULE_V_TILES,
+                       v_tiles=4)
+    assert _code(kw) == 0, kda.load().kda_last_error()
+    kw["work_counter"] = big[:wl.B * wl.H]          # one element short
+    assert _code(kw) == _abi.KDA_E_ARG
+    assert b"1 + batch * heads" in kda.load().kda_last_error()
+    kw["work_counter"] = big
+    for bad in (1, 3, 16, -2):
+        kw["v_tiles"] = bad
+        assert _code(kw) == _abi.KDA_E_ARG
+    kw["v_tiles"] = 0                               # library's choice
+    assert _code(kw) == 0
+    kw["pending_lens"] = torch.zeros(wl.B, dtype=torch.int32)
+    assert _code(kw) == _abi.KDA_E_UNSUPPORTED
+    wl = make_workload("ragged", B=4, H=2, D=16, Q=4, N=8)
+    kw = verify_kwargs(wl, 0, torch.zeros(1 + 8, dtype=torch.int32),
+                       schedule=_abi.KDA_SCHEDULE_V_TILES)
+    assert _code(kw) == _abi.KDA_E_UNSUPPORTED       # head dim 16
+    wl = make_workload("ragged", B=4, H=2, D=64, Q=12, N=8)
+    kw = verify_kwargs(wl, 0, torch.zeros(1 + 8, dtype=torch.int32),
+                       schedule=_abi.KDA_SCHEDULE_V_TILES)
+    assert _code(kw) == _abi.KDA_E_UNSUPPORTED       # window 12
+    # the unfused verify needs no counter for V-tiles
+    wl = make_workload("ragged", B=4, H=2, D=64, Q=4, N=8)
+    kw = verify_kwargs(wl, 0, None, schedule=_abi.KDA_SCHEDULE_V_TILES)
+    for k in ("conv_state", "conv_weight", "num_accepted_tokens"):
+        kw[k] = None
+    assert kda.check_verify_qkv(**kw) == 0, kda.load().kda_last_error()

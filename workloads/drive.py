@@ -15,9 +15,16 @@ import linear_attention_speculative_amd as kda
 from .gen import Workload
 
 
+def counter(wl: Workload, device="cuda") -> torch.Tensor:
+    """A zeroed work-counter array for any verify schedule of `wl`: the
+    ticket counter plus one arrival counter per (request, head)."""
+    return torch.zeros(1 + wl.B * wl.H, dtype=torch.int32, device=device)
+
+
 def verify_kwargs(wl: Workload, layer: int, counter: torch.Tensor,
                   max_workgroups: int = 0, items_per_ticket: int = 0,
-                  schedule: int = 0, pending_lens=None) -> dict:
+                  schedule: int = 0, pending_lens=None,
+                  v_tiles: int = 0) -> dict:
     L = wl.layers[layer]
     return dict(
         mixed_qkv=L.mixed_qkv, raw_gate=L.raw_gate, raw_beta=L.raw_beta,
@@ -31,16 +38,17 @@ def verify_kwargs(wl: Workload, layer: int, counter: torch.Tensor,
         work_counter=counter, record_rows=wl.record_rows,
         null_block_id=wl.null_block_id, max_workgroups=max_workgroups,
         items_per_ticket=items_per_ticket, schedule=schedule,
-        pending_lens=pending_lens)
+        pending_lens=pending_lens, v_tiles=v_tiles)
 
 
 def verify(wl: Workload, layer: int, counter: torch.Tensor,
            max_workgroups: int = 0, items_per_ticket: int = 0,
-           stream=None, schedule: int = 0, pending_lens=None) -> None:
+           stream=None, schedule: int = 0, pending_lens=None,
+           v_tiles: int = 0) -> None:
     kda.conv_update_verify(stream=stream,
                            **verify_kwargs(wl, layer, counter,
                                            max_workgroups, items_per_ticket,
-                                           schedule, pending_lens))
+                                           schedule, pending_lens, v_tiles))
 
 
 def verify_qkv_kwargs(wl: Workload, layer: int, mixed_qkv: torch.Tensor,

@@ -82,8 +82,7 @@ def snapshot(wl, layer: int, reqs=None) -> Sample:
     idx = torch.tensor([0] + live_slots, device=dev)
     ridx = torch.tensor(rec_index if rec_index else [0], device=dev)
     tok_all = [t for ts in tok for t in ts]
-    tidx = torch.tensor(tok_all if tok_all else [0], device=dev,
-                        dtype=torch.long)
+    tidx = torch.tensor(tok_all, device=dev, dtype=torch.long)
     state = f64(L.state.index_select(0, idx))
     state[0] = 0.0
     conv = f64(wl.conv_state_dim_first(layer).index_select(0, idx))
@@ -91,7 +90,10 @@ def snapshot(wl, layer: int, reqs=None) -> Sample:
     kg = f64(L.key_gate.index_select(0, ridx))
     if not rec_index:
         corr, kg = corr[:0], kg[:0]
-    take = (lambda t: f64(t.index_select(0, tidx))[:len(tok_all)])
+    # (no index_select at all when there are no tokens: the activation
+    # tensors may then have no rows)
+    take = (lambda t: f64(t.index_select(0, tidx)) if tok_all else
+            np.zeros((0,) + tuple(t.shape[1:])))
     new_qsl = np.concatenate([[0], np.cumsum([len(ts) for ts in tok])])
     inputs = dict(
         mixed_qkv=take(L.mixed_qkv), raw_gate=take(L.raw_gate),
