@@ -79,9 +79,9 @@ COLD_WORKLOADS = ("ragged",)
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 ALIGN_BLOCK_SIZE = 16          # tokens per state block, align workload
 KERNEL_SOURCES = {
-    "kda_verify_grid_kernel": "kda_verify.hip",
-    "kda_verify_vtile_kernel": "kda_verify.hip",
-    "kda_verify_kernel": "kda_verify.hip",
+    "kda_verify_grid_kernel": "kda_verify_kernels.hpp",
+    "kda_verify_vtile_kernel": "kda_verify_kernels.hpp",
+    "kda_verify_kernel": "kda_verify_kernels.hpp",
     "kda_commit_grid_kernel": "kda_commit.hip",
 }
 
@@ -156,17 +156,12 @@ SCHEDULES = {"default": 0, "per-item": 1, "tickets": 2, "v-tiles": 3}
 
 
 def verify_kernel(wl, schedule: int, v_tiles: int) -> str:
-    """Name of the kernel the plain verify of `wl` launches: V-tiles when
-    asked for, or by default (the library's rule, given a counter with one
-    arrival slot per item) for head dims 64/128, windows up to 8 and at most
-    256 (request, head) items; else one workgroup per item."""
+    """Name of the kernel the plain verify of `wl` launches (the default
+    schedule runs one workgroup per item up to 65535 requests)."""
     if schedule == SCHEDULES["v-tiles"]:
         return "kda_verify_vtile_kernel"
-    if schedule == SCHEDULES["tickets"]:
+    if schedule == SCHEDULES["tickets"] or wl.B > 65535:
         return "kda_verify_kernel"
-    if (schedule == 0 and wl.D in (64, 128) and wl.Q <= 8 and
-            (v_tiles > 1 or wl.B * wl.H <= 256)):
-        return "kda_verify_vtile_kernel"
     return "kda_verify_grid_kernel"
 
 

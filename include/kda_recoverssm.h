@@ -98,7 +98,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 /* How the verify hands out its (request, head) work items. */
 typedef enum {
   KDA_SCHEDULE_DEFAULT = 0,    /* the library's choice (the fastest measured
-                                  for the shape) */
+                                  for the shape: PER_ITEM up to 65535
+                                  requests, else TICKETS) */
   KDA_SCHEDULE_PER_ITEM = 1,   /* one workgroup per item, handed out by the
                                   hardware dispatcher (each XCD takes one
                                   contiguous eighth of the items) */
@@ -194,8 +195,7 @@ typedef struct {
                               (batch <= 65535). */
   int32_t work_counter_len; /* elements of work_counter; 0 with a counter
                                means 1.  The V-tile schedule of the fused
-                               conv verify needs 1 + batch * H (the default
-                               schedule only picks V-tiles when it is). */
+                               conv verify needs 1 + batch * H. */
   int32_t v_tiles;         /* V-tile schedule: 2, 4 or 8 workgroups per
                               (request, head); 0 = the library's choice */
 } kda_verify_args;

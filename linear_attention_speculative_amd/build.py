@@ -20,7 +20,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libkda_recoverssm.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["kda_verify.hip", "kda_commit.hip", "kda_plan.hip", "kda_api.cpp"]
+SOURCES = ["kda_verify_d128.hip", "kda_verify_d64.hip", "kda_verify_d32.hip",
+           "kda_verify_d16.hip", "kda_verify.hip", "kda_commit.hip",
+           "kda_plan.hip", "kda_api.cpp"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU ops are disabled for all device code.

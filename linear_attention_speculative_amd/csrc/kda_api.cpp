@@ -77,12 +77,11 @@ struct VerifyPlan {
   int schedule = 0;
 };
 
-// V-tiles per (request, head) item that the default schedule uses for
-// `items` items (1: whole items): enough workgroups to cover the compute
-// units when the items alone would not.  `floor`: the least value returned.
-int default_vtiles(int64_t items, int floor) {
-  int vt = items <= 64 ? 8 : items <= 128 ? 4 : items <= 256 ? 2 : 1;
-  return vt < floor ? floor : vt;
+// V-tiles per (request, head) item for the V-tile schedule when the caller
+// leaves the count to the library: enough workgroups to cover the compute
+// units when the items alone would not.
+int default_vtiles(int64_t items) {
+  return items <= 64 ? 8 : items <= 128 ? 4 : 2;
 }
 
 #define KDA_TRY(expr)             \
@@ -93,8 +92,11 @@ int default_vtiles(int64_t items, int floor) {
 
 // conv: the fused conv update (kda_conv_update_verify); otherwise mixed_qkv
 // already holds the convolved q | k | v (kda_recoverssm_verify_qkv) and the
-// conv state, taps and accepted counts are not used.
-int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
+// conv state, taps and accepted counts are not used.  scratch_len > 0: the
+// library supplies the work counters (that many), a->work_counter is
+// ignored and plan->p.counter is left for the caller to set.
+int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv,
+                int64_t scratch_len = 0) {
   if (a == nullptr) return fail(KDA_E_ARG, "verify arguments are NULL");
   if (a->batch < 0) return fail(KDA_E_ARG, "batch is negative");
   const int64_t Q = a->spec_query_len;
@@ -291,7 +293,8 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
       return fail(KDA_E_ARG,
                   "query_start_loc, state_indices and num_accepted_tokens "
                   "are required");
-    if (!a->work_counter && a->schedule == KDA_SCHEDULE_TICKETS)
+    if (!a->work_counter && scratch_len == 0 &&
+        a->schedule == KDA_SCHEDULE_TICKETS)
       return fail(KDA_E_ARG, "the ticket schedule needs a work_counter");
     if (a->pending_lens && a->batch > 65535)
       return fail(KDA_E_UNSUPPORTED,
@@ -299,7 +302,8 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
                   "supports at most 65535 requests");
     const void* ptrs[] = {a->query_start_loc, a->state_indices,
                           a->num_accepted_tokens, a->record_rows,
-                          a->work_counter, a->pending_lens};
+                          scratch_len > 0 ? nullptr : a->work_counter,
+                          a->pending_lens};
     for (const void* q : ptrs)
       if (q && !aligned(q, 4))
         return fail(KDA_E_UNALIGNED, "metadata pointers must be 4-byte "
@@ -369,7 +373,7 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
   p.accepted = conv ? a->num_accepted_tokens : a->state_indices;
   p.record_rows = a->record_rows;
   p.pending = a->pending_lens;
-  p.counter = a->work_counter;
+  p.counter = scratch_len > 0 ? nullptr : a->work_counter;
   p.B = a->batch;
   p.H = int32_t(H);
   p.Q = int32_t(Q);
@@ -397,9 +401,10 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
   // V-tiles: possible for head dims 64 and 128 and windows up to 8 without
   // the deferred flush; the fused conv needs one arrival counter per item.
   const int64_t counter_len =
-      a->work_counter == nullptr ? 0
-                                 : (a->work_counter_len > 0 ? a->work_counter_len
-                                                            : 1);
+      scratch_len > 0 ? scratch_len
+      : a->work_counter == nullptr
+          ? 0
+          : (a->work_counter_len > 0 ? a->work_counter_len : 1);
   const int64_t items = int64_t(a->batch) * H;
   const bool vt_shape = (D == 64 || D == 128) && Q <= 8 &&
                         a->pending_lens == nullptr;
@@ -411,18 +416,25 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv) {
       return fail(KDA_E_UNSUPPORTED,
                   "the V-tile schedule supports head dims 64 and 128, "
                   "windows up to 8 and no pending_lens");
+    if (!vt_counter && scratch_len > 0)
+      return fail(KDA_E_CAPACITY,
+                  "the allocation-free verify's scratch holds %lld "
+                  "counters; V-tiles of %lld (request, head) items need "
+                  "%lld",
+                  (long long)scratch_len, (long long)items,
+                  (long long)(1 + items));
     if (!vt_counter)
       return fail(KDA_E_ARG,
                   "the V-tile schedule of the fused conv verify needs a "
                   "work_counter of 1 + batch * heads = %lld elements",
                   (long long)(1 + items));
-    if (vt == 0) vt = default_vtiles(items, 8);
-    if (vt <= 1) vt = 2;
-  } else if (schedule == KDA_SCHEDULE_DEFAULT && vt_shape && vt_counter) {
-    // small batches: V-tiles where whole items would leave CUs idle
-    vt = vt != 0 ? vt : default_vtiles(items, 1);
-    if (vt > 1) schedule = KDA_SCHEDULE_V_TILES;
+    if (vt == 0) vt = default_vtiles(items);
   }
+  // The default schedule never takes V-tiles: measured on MI355X they are
+  // not faster than whole items at any batch (one request: 8.2 us per
+  // verify either way; 64 requests: 41.0 us whole, 41.6 us with 2 tiles).
+  // The verify of a small batch is bound by the latency of its phases,
+  // which splitting the rows does not shorten.
   if (schedule == KDA_SCHEDULE_V_TILES && items * vt > 0x7fffffff)
     return fail(KDA_E_CAPACITY, "batch * heads * v_tiles exceeds 2^31");
   p.v_tiles = schedule == KDA_SCHEDULE_V_TILES ? vt : 0;

@@ -130,9 +130,15 @@ constexpr int kScheduleVTiles = 3;
 // workgroups as are resident at once.
 int launch_verify(const VerifyParams& p, int D, bool act_bf16, int schedule,
                   int grid, hipStream_t stream);
+// The verify launches of one head dim (16, 32, 64, 128), each defined in
+// its own translation unit.
+template <int D>
+int launch_verify_dim(const VerifyParams& p, bool act_bf16, int schedule,
+                      int grid, hipStream_t stream);
 int launch_commit(const CommitParams& p, int D, hipStream_t stream);
 int launch_commit_plan(const PlanParams& p, hipStream_t stream);
 int launch_compact(const CompactParams& p, int elem_bytes, hipStream_t stream);
 int launch_reset_counter(int32_t* counter, int n, hipStream_t stream);
+
 
 }  // namespace kda

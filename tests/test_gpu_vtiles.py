@@ -65,16 +65,16 @@ def test_vtiles_bitwise_equal_per_item(case):
 
 def test_single_request_vtiles_matches_oracle():
     """The single-request workload (B=1, 32 heads, head dim 128, token-first
-    conv) under each V-tile count and the default schedule (which takes
-    V-tiles here): outputs, records, conv roll and the commit against the
-    oracle."""
+    conv) under each V-tile count (0: the library's count, 8 here) and the
+    default schedule: outputs, records, conv roll and the commit against
+    the oracle."""
     for vt in (0, 2, 4, 8):
         wl = make_workload("single", DEV)
         L = wl.layers[0]
         sample = snapshot(wl, 0)
         state0 = L.state.clone()
         c = drive.counter(wl)
-        drive.verify(wl, 0, c, schedule=V_TILES if vt else 0, v_tiles=vt)
+        drive.verify(wl, 0, c, schedule=V_TILES, v_tiles=vt)
         torch.cuda.synchronize()
         assert int(c.abs().sum()) == 0
         assert torch.equal(L.state, state0), "verify wrote the checkpoint"
@@ -120,9 +120,10 @@ def test_vtiles_graph_replay_and_counter_reuse():
         assert torch.equal(L.page, eager_page)
 
 
-def test_default_schedule_needs_counter_room_for_vtiles():
-    """With a one-element counter the default schedule cannot take V-tiles
-    for the fused conv verify and runs whole items, with the same bytes."""
+def test_vtiles_need_counter_room():
+    """The default schedule runs whole items with a one-element counter and
+    gives the same bytes as with a full counter array; the V-tile schedule
+    refuses a counter without one arrival slot per item."""
     wl = make_workload("single", DEV)
     L = wl.layers[0]
     page0 = L.page.clone()
