@@ -345,6 +345,19 @@ int kda_check_verify(const kda_verify_args* args);
    unchanged; null requests get +0.0 outputs and nothing else. */
 int kda_conv_update_verify(const kda_verify_args* args, void* stream);
 
+/* kda_conv_update_verify for callers that cannot allocate device memory
+   (code under HIP graph capture, tight serving loops, harnesses that forbid
+   allocation): the same checks, kernels and results, except that the work
+   counters (the ticket counter, and the V-tile schedule's arrival counters)
+   live in a scratch array of the library instead of args->work_counter,
+   which is ignored.  The array holds 1 + 65536 int32 per GPU, is looked up
+   (and cleared by a kernel on `stream`) on the first call on each device,
+   and is kept until the process ends.  Every launch leaves it at zero, but
+   it is shared: calls that overlap on one GPU (two streams, or two threads)
+   race on it.  A V-tile launch of more than 65536 (request, head) items is
+   refused with KDA_E_CAPACITY before any device call.  Allocates nothing. */
+int kda_conv_update_verify_noalloc(const kda_verify_args* args, void* stream);
+
 /* The unfused verify (ops page, `kda_recoverssm_verify` and
    `_kda_recoverssm_verify_kernel`): the same as kda_conv_update_verify
    except that mixed_qkv [T, 3HD] already holds the convolved q | k | v

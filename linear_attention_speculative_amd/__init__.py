@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     check_verify,
     check_verify_qkv,
     conv_update_verify,
+    conv_update_verify_noalloc,
     describe,
     reset_counter,
     verify_args,

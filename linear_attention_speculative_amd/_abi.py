@@ -30,7 +30,8 @@ KDA_BF16 = 1
 
 EXPORTED = (
     "kda_abi_version", "kda_last_error", "kda_status_string",
-    "kda_check_verify", "kda_conv_update_verify", "kda_check_verify_qkv",
+    "kda_check_verify", "kda_conv_update_verify",
+    "kda_conv_update_verify_noalloc", "kda_check_verify_qkv",
     "kda_recoverssm_verify_qkv", "kda_check_commit",
     "kda_recoverssm_commit", "kda_check_commit_plan", "kda_commit_plan",
     "kda_check_compact_conv", "kda_compact_conv_state",
@@ -143,6 +144,9 @@ def load() -> ctypes.CDLL:
     lib.kda_check_verify.argtypes = [POINTER(KdaVerifyArgs)]
     lib.kda_conv_update_verify.restype = c_int
     lib.kda_conv_update_verify.argtypes = [POINTER(KdaVerifyArgs), c_void_p]
+    lib.kda_conv_update_verify_noalloc.restype = c_int
+    lib.kda_conv_update_verify_noalloc.argtypes = [POINTER(KdaVerifyArgs),
+                                                   c_void_p]
     lib.kda_check_verify_qkv.restype = c_int
     lib.kda_check_verify_qkv.argtypes = [POINTER(KdaVerifyArgs)]
     lib.kda_recoverssm_verify_qkv.restype = c_int

@@ -812,6 +812,27 @@ int kda_conv_update_verify(const kda_verify_args* args, void* stream) {
       "kda_conv_update_verify launch");
 }
 
+int kda_conv_update_verify_noalloc(const kda_verify_args* args,
+                                   void* stream) {
+  g_err.clear();
+  // Every host check first (with the scratch standing in for the counter
+  // array), so that a batch the scratch cannot serve is refused before any
+  // device call.
+  VerifyPlan plan;
+  KDA_TRY(plan_verify(args, &plan, true, kda::kScratchCounters));
+  if (plan.noop) return KDA_OK;
+  int32_t* counters = nullptr;
+  const int e = kda::scratch_counters(static_cast<hipStream_t>(stream),
+                                      &counters);
+  if (e != 0)
+    return device_status(e, "kda_conv_update_verify_noalloc scratch");
+  plan.p.counter = counters;
+  return device_status(
+      kda::launch_verify(plan.p, plan.D, plan.act_bf16, plan.schedule,
+                         plan.grid, static_cast<hipStream_t>(stream)),
+      "kda_conv_update_verify_noalloc launch");
+}
+
 int kda_check_commit(const kda_commit_args* args) {
   g_err.clear();
   CommitPlan plan;

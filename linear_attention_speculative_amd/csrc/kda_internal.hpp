@@ -140,5 +140,12 @@ int launch_commit_plan(const PlanParams& p, hipStream_t stream);
 int launch_compact(const CompactParams& p, int elem_bytes, hipStream_t stream);
 int launch_reset_counter(int32_t* counter, int n, hipStream_t stream);
 
+// The allocation-free verify's counters: kScratchCounters int32 in a
+// per-GPU array of the library (the ticket counter, then one arrival
+// counter per (request, head)).  Sets *out to the current device's copy;
+// the first call on a device looks its address up and clears it with a
+// kernel on `stream`.
+constexpr int kScratchCounters = 1 + 65536;
+int scratch_counters(hipStream_t stream, int32_t** out);
 
 }  // namespace kda

@@ -139,6 +139,19 @@ def conv_update_verify(*, stream=None, **kwargs) -> None:
         _raise(rc)
 
 
+def conv_update_verify_noalloc(*, stream=None, **kwargs) -> None:
+    """`conv_update_verify` without a caller-supplied counter array: the
+    library's per-GPU scratch holds the work counters (the C entry point
+    allocates nothing; `work_counter` is ignored).  Calls that overlap on
+    one GPU race on that scratch."""
+    kwargs.setdefault("work_counter", None)
+    a = verify_args(**kwargs)
+    rc = _abi.load().kda_conv_update_verify_noalloc(ctypes.byref(a),
+                                                   _stream(stream))
+    if rc != _abi.KDA_OK:
+        _raise(rc)
+
+
 def _qkv_args(kwargs) -> _abi.KdaVerifyArgs:
     for k in ("conv_state", "conv_weight", "num_accepted_tokens"):
         kwargs.setdefault(k, None)
