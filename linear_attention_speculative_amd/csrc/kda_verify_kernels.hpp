@@ -318,13 +318,16 @@ __device__ __forceinline__ void history3(
     const Small<D, QMAX, ACT_BF16, DV>& s, int jj,
     typename Act<ACT_BF16>::T (&hv)[3]) {
   using AT = typename Act<ACT_BF16>::T;
-  hv[0] = s.hist[jj][0];
-  hv[1] = s.hist[jj][1];
-  hv[2] = s.hist[jj][2];
+  // each path reads only the registers its loads filled (the other set is
+  // never written for this item)
   if (p.flags & kConvRow) {
     hv[0] = row_at<AT, 0, QMAX>(s.row[jj], it.a - 1);
     hv[1] = row_at<AT, 1, QMAX>(s.row[jj], it.a - 1);
     hv[2] = row_at<AT, 2, QMAX>(s.row[jj], it.a - 1);
+  } else {
+    hv[0] = s.hist[jj][0];
+    hv[1] = s.hist[jj][1];
+    hv[2] = s.hist[jj][2];
   }
 }
 
