@@ -15,10 +15,14 @@ HBM).
 Prints one JSON line.  `value` is verified tokens per second (draft tokens
 verified per step / step time over K back-to-back steps, timed as one
 replay of a HIP graph that holds the K steps; `ms_per_step_eager` is the
-same K steps launched one by one, `--eager` reports that instead); `roofline`
-describes the kernel that takes the most time per step, from HIP events
-around its launches; `kernels` gives each kernel's median, p10 and p90 over
-the timed steps, the median of single synchronized launches, and the
+same K steps launched one by one with nothing between the launches,
+`--eager` reports that instead); `roofline` describes the kernel that takes
+the most time per step, from HIP events that the library records from the
+kernels' own dispatch (kda_set_launch_events: an event recorded on the
+stream between two launches adds its marker's gap, 6-11 us here, to the
+kernel it brackets), over K more eager steps; `kernels` gives each kernel's
+median, p10 and p90 over those steps, the median of single synchronized
+launches, and the
 median of single launches that each follow an untimed 1 GiB write (which
 evicts the caches), so that any help from the last-level cache between
 kernels shows up as a difference; `cpu_baseline`
@@ -53,7 +57,8 @@ Other workloads (`--workload`), each one JSON line of the same form:
             untimed 1 GiB write that evicts it.
 The default run (headline) is the one the throughput figure is quoted on.
 `--cold-steps` times any workload that way (an evicting write before every
-timed step, events around the step's launches only).
+timed step, the step timed from its first kernel's start to its last
+kernel's end).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold-steps]
   python bench.py --copy-calibration   # plain copy for HBM counter scaling
@@ -403,35 +408,62 @@ def main() -> int:
     evict = torch.empty(EVICT_BYTES // 4, dtype=torch.float32,
                         device="cuda") if cold_steps else None
 
+    from linear_attention_speculative_amd import set_launch_events
+
     def step(ev=None):
-        for i, (_, _, _, fn) in enumerate(phases):
+        # ev: per phase a (start, stop) pair of events that the library
+        # records from the kernels' own dispatch (the first launch's start,
+        # the last launch's end); an event recorded on the stream between
+        # launches would add its marker's gap to the kernel it brackets
+        for i, (_, _, n, fn) in enumerate(phases):
             if ev is not None:
-                ev[i].record()
+                set_launch_events(ev[i][0], ev[i][1], n)
             fn()
-        if ev is not None:
-            ev[P].record()
+            if ev is not None and set_launch_events(None, None, 0) != 0:
+                raise RuntimeError(f"phase {phases[i][0]} launched fewer "
+                                   f"than {n} kernels")
+
+    def new_events():
+        out = []
+        for _ in range(P):
+            pair = (torch.cuda.Event(enable_timing=True),
+                    torch.cuda.Event(enable_timing=True))
+            for e in pair:
+                e.record()                 # creates the event
+            out.append(pair)
+        return out
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(P + 1)]
-              for _ in range(args.steps)]
+    # The step time: K eager steps with nothing between the launches (cold
+    # steps: each after an untimed cache-evicting write, timed from its
+    # first kernel's start to its last kernel's end).
+    events = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         if evict is not None:
-            evict.fill_(float(k))          # untimed: before the first event
-        step(events[k])
+            evict.fill_(float(k))          # untimed: before the first kernel
+            step(events[k])
+        else:
+            step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     if evict is not None:
-        # cold steps: the time between each step's first and last event
-        ms_step = sum(e[0].elapsed_time(e[P]) for e in events) / args.steps
+        ms_step = sum(e[0][0].elapsed_time(e[P - 1][1])
+                      for e in events) / args.steps
+    else:
+        # per-kernel durations: K more steps with every phase's launches
+        # timed from their own dispatch
+        for k in range(args.steps):
+            step(events[k])
+        torch.cuda.synchronize()
     # per phase: microseconds per launch (a phase of n launches / n)
-    per = [sorted(e[i].elapsed_time(e[i + 1]) * 1e3 / phases[i][2]
+    per = [sorted(e[i][0].elapsed_time(e[i][1]) * 1e3 / phases[i][2]
                   for e in events) for i in range(P)]
     mean_ms = [sum(x) / args.steps / 1e3 for x in per]
     print(f"# timed {args.steps} steps: {ms_step:.4f} ms/step ("
@@ -480,25 +512,25 @@ def main() -> int:
     scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     cold = [[] for _ in range(P)]
     iso = [[] for _ in range(P)]
+    def timed(fn, n):
+        """One phase, its launches timed from their own dispatch."""
+        ev = new_events()[0]
+        set_launch_events(ev[0], ev[1], n)
+        fn()
+        if set_launch_events(None, None, 0) != 0:
+            raise RuntimeError("a phase launched fewer kernels than armed")
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / n
+
     for k in range(args.cold):
         for i, (_, _, n, fn) in enumerate(phases):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             scratch.fill_(float(k) + 0.5 * i)
-            ev[0].record()
-            fn()
-            ev[1].record()
-            torch.cuda.synchronize()
-            cold[i].append(ev[0].elapsed_time(ev[1]) * 1e3 / n)
+            cold[i].append(timed(fn, n))
     del scratch
     for k in range(args.cold):
         for i, (_, _, n, fn) in enumerate(phases):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             torch.cuda.synchronize()
-            ev[0].record()
-            fn()
-            ev[1].record()
-            torch.cuda.synchronize()
-            iso[i].append(ev[0].elapsed_time(ev[1]) * 1e3 / n)
+            iso[i].append(timed(fn, n))
     for xs in cold + iso:
         xs.sort()
 

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 /* Status codes. */
 typedef enum {
@@ -416,6 +416,23 @@ int kda_recoverssm_commit_step(const kda_commit_args* commit,
    (for a counter left non-zero by an aborted launch).  Uses no memset
    node, so it may be captured in a graph. */
 int kda_reset_counter(int32_t* counter, int32_t n, void* stream);
+
+/* Kernel timing without a profiler, for callers that measure each kernel's
+   own duration (an event recorded on the stream around a launch also counts
+   the gap the event's own marker adds before the next dispatch).  Arms the
+   calling thread: the next `launches` verify, commit, plan or compaction
+   kernels that library calls on this thread launch are dispatched with
+   hipExtLaunchKernel, `start_event` (a hipEvent_t, may be NULL) recording
+   the start of the first of them and `stop_event` (may be NULL) the end of
+   the last.  The counter-clearing kernels (kda_reset_counter, the first
+   use of the no-allocation entry point's array on a device) are not
+   counted.  launches = 0 disarms.  If `pending` is not NULL it receives
+   the number of launches the previous arming was still waiting for (0 when
+   every armed launch happened, so its stop event was recorded).  The
+   events stay the caller's; do not arm the thread while it captures a
+   graph.  KDA_E_ARG if launches < 0 (the previous arming is then kept). */
+int kda_set_launch_events(void* start_event, void* stop_event,
+                          int32_t launches, int32_t* pending);
 
 #ifdef __cplusplus
 }

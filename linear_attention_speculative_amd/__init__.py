@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     conv_update_verify_noalloc,
     describe,
     reset_counter,
+    set_launch_events,
     verify_args,
     verify_qkv,
 )

@@ -36,7 +36,7 @@ EXPORTED = (
     "kda_recoverssm_commit", "kda_check_commit_plan", "kda_commit_plan",
     "kda_check_compact_conv", "kda_compact_conv_state",
     "kda_check_commit_step", "kda_recoverssm_commit_step",
-    "kda_reset_counter",
+    "kda_reset_counter", "kda_set_launch_events",
 )
 
 
@@ -175,5 +175,8 @@ def load() -> ctypes.CDLL:
                                                c_void_p]
     lib.kda_reset_counter.restype = c_int
     lib.kda_reset_counter.argtypes = [c_void_p, c_int32, c_void_p]
+    lib.kda_set_launch_events.restype = c_int
+    lib.kda_set_launch_events.argtypes = [c_void_p, c_void_p, c_int32,
+                                          POINTER(c_int32)]
     _LIB = lib
     return lib

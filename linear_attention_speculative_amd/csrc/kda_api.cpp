@@ -12,6 +12,15 @@
 #include "kda_internal.hpp"
 #include "kda_recoverssm.h"
 
+namespace kda {
+
+LaunchTiming& launch_timing() {
+  thread_local LaunchTiming t;
+  return t;
+}
+
+}  // namespace kda
+
 namespace {
 
 thread_local std::string g_err;
@@ -902,6 +911,19 @@ int kda_recoverssm_commit_step(const kda_commit_args* commit,
   return device_status(
       kda::launch_commit(cp.p, cp.D, static_cast<hipStream_t>(stream)),
       "kda_recoverssm_commit_step launch");
+}
+
+int kda_set_launch_events(void* start_event, void* stop_event,
+                          int32_t launches, int32_t* pending) {
+  g_err.clear();
+  if (launches < 0)
+    return fail(KDA_E_ARG, "kda_set_launch_events needs launches >= 0");
+  kda::LaunchTiming& t = kda::launch_timing();
+  if (pending) *pending = t.remaining;
+  t.start = launches > 0 ? static_cast<hipEvent_t>(start_event) : nullptr;
+  t.stop = launches > 0 ? static_cast<hipEvent_t>(stop_event) : nullptr;
+  t.remaining = launches;
+  return KDA_OK;
 }
 
 int kda_reset_counter(int32_t* counter, int32_t n, void* stream) {

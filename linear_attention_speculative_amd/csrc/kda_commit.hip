@@ -421,13 +421,13 @@ int launch_cqa(const CommitParams& p, hipStream_t stream) {
   const int64_t items = int64_t(p.L) * p.B * p.H;
   if (items > 0x7fffffff) return int(hipErrorInvalidValue);
   if (p.grid <= 0 && p.B <= 65535 && p.L <= 65535) {
-    hipLaunchKernelGGL((kda_commit_grid_kernel<D, QMAX, ALIGN, STEP>),
-                       dim3(p.H, p.B, p.L), dim3(C::NT), 0, stream, p);
+    launch_kernel((kda_commit_grid_kernel<D, QMAX, ALIGN, STEP>),
+                  dim3(p.H, p.B, p.L), dim3(C::NT), 0, stream, p);
   } else {
     const int64_t g = p.grid > 0 ? p.grid : 4096;
-    hipLaunchKernelGGL((kda_commit_strided_kernel<D, QMAX, ALIGN, STEP>),
-                       dim3(unsigned(g < items ? g : items)), dim3(C::NT), 0,
-                       stream, p);
+    launch_kernel((kda_commit_strided_kernel<D, QMAX, ALIGN, STEP>),
+                  dim3(unsigned(g < items ? g : items)), dim3(C::NT), 0,
+                  stream, p);
   }
   return int(hipGetLastError());
 }

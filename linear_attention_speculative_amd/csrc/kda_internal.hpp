@@ -2,10 +2,38 @@
 // kernels.  Not part of the public ABI (see include/kda_recoverssm.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace kda {
+
+// Timing armed by kda_set_launch_events on the calling thread: the next
+// `remaining` launches made through launch_kernel are dispatched with
+// hipExtLaunchKernel, `start` on the first and `stop` on the last.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+  int remaining = 0;
+};
+LaunchTiming& launch_timing();
+
+// Launch of a verify, commit, plan or compaction kernel.
+template <typename... Args, typename F>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem,
+                          hipStream_t stream, Args... args) {
+  LaunchTiming& t = launch_timing();
+  if (t.remaining <= 0) {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, args...);
+    return;
+  }
+  hipEvent_t start = t.start;
+  hipEvent_t stop = t.remaining == 1 ? t.stop : nullptr;
+  t.start = nullptr;
+  if (--t.remaining == 0) t.stop = nullptr;
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, start, stop, 0,
+                        args...);
+}
 
 constexpr int kConvWidth = 4;   // taps of the short convolution
 constexpr int kMaxWindow = 16;  // largest draft window Q supported

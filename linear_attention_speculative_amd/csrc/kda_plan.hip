@@ -61,8 +61,8 @@ __global__ void __launch_bounds__(kCompactThreads)
 int launch_commit_plan(const PlanParams& p, hipStream_t stream) {
   if (p.B <= 0) return 0;
   const int blocks = (p.B + kPlanThreads - 1) / kPlanThreads;
-  hipLaunchKernelGGL(kda_commit_plan_kernel, dim3(blocks), dim3(kPlanThreads),
-                     0, stream, p);
+  launch_kernel(kda_commit_plan_kernel, dim3(blocks), dim3(kPlanThreads),
+                0, stream, p);
   return int(hipGetLastError());
 }
 
@@ -71,11 +71,11 @@ int launch_compact(const CompactParams& p, int elem_bytes, hipStream_t stream) {
   if (p.B > 65535 || p.L > 65535) return int(hipErrorInvalidValue);
   const dim3 grid((p.C + kCompactThreads - 1) / kCompactThreads, p.B, p.L);
   if (elem_bytes == 2)
-    hipLaunchKernelGGL(kda_compact_conv_kernel<uint16_t>, grid,
-                       dim3(kCompactThreads), 0, stream, p);
+    launch_kernel(kda_compact_conv_kernel<uint16_t>, grid,
+                  dim3(kCompactThreads), 0, stream, p);
   else if (elem_bytes == 4)
-    hipLaunchKernelGGL(kda_compact_conv_kernel<uint32_t>, grid,
-                       dim3(kCompactThreads), 0, stream, p);
+    launch_kernel(kda_compact_conv_kernel<uint32_t>, grid,
+                  dim3(kCompactThreads), 0, stream, p);
   else
     return int(hipErrorInvalidValue);
   return int(hipGetLastError());

@@ -1212,19 +1212,19 @@ int launch_vtiles(const VerifyParams& p, int vt, hipStream_t stream) {
     if (n > 0x7fffffff) return int(hipErrorInvalidConfiguration);
     switch (vt) {
       case 2:
-        hipLaunchKernelGGL((kda_verify_vtile_kernel<D, QMAX, ACT_BF16, D / 2>),
-                           dim3(unsigned(n)),
-                           dim3(VerifyCfg<D, QMAX, D / 2>::NT), 0, stream, p);
+        launch_kernel((kda_verify_vtile_kernel<D, QMAX, ACT_BF16, D / 2>),
+                      dim3(unsigned(n)),
+                      dim3(VerifyCfg<D, QMAX, D / 2>::NT), 0, stream, p);
         return int(hipGetLastError());
       case 4:
-        hipLaunchKernelGGL((kda_verify_vtile_kernel<D, QMAX, ACT_BF16, D / 4>),
-                           dim3(unsigned(n)),
-                           dim3(VerifyCfg<D, QMAX, D / 4>::NT), 0, stream, p);
+        launch_kernel((kda_verify_vtile_kernel<D, QMAX, ACT_BF16, D / 4>),
+                      dim3(unsigned(n)),
+                      dim3(VerifyCfg<D, QMAX, D / 4>::NT), 0, stream, p);
         return int(hipGetLastError());
       case 8:
-        hipLaunchKernelGGL((kda_verify_vtile_kernel<D, QMAX, ACT_BF16, D / 8>),
-                           dim3(unsigned(n)),
-                           dim3(VerifyCfg<D, QMAX, D / 8>::NT), 0, stream, p);
+        launch_kernel((kda_verify_vtile_kernel<D, QMAX, ACT_BF16, D / 8>),
+                      dim3(unsigned(n)),
+                      dim3(VerifyCfg<D, QMAX, D / 8>::NT), 0, stream, p);
         return int(hipGetLastError());
       default:
         return int(hipErrorInvalidValue);
@@ -1242,15 +1242,15 @@ int launch_one(const VerifyParams& p, int schedule, int grid,
   // carries no loop state, which the ticket loop pays for in registers.
   if (p.pending != nullptr) {  // the deferred flush: per-item kernel only
     if (p.B > 65535) return int(hipErrorInvalidConfiguration);
-    hipLaunchKernelGGL((kda_verify_grid_kernel<D, QMAX, ACT_BF16, true>),
-                       dim3(p.H, p.B), dim3(C::NT), 0, stream, p);
+    launch_kernel((kda_verify_grid_kernel<D, QMAX, ACT_BF16, true>),
+                  dim3(p.H, p.B), dim3(C::NT), 0, stream, p);
     return int(hipGetLastError());
   }
   if (schedule == kScheduleVTiles && p.v_tiles > 1)
     return launch_vtiles<D, QMAX, ACT_BF16>(p, p.v_tiles, stream);
   if (schedule != kScheduleTickets && p.B <= 65535) {
-    hipLaunchKernelGGL((kda_verify_grid_kernel<D, QMAX, ACT_BF16, false>),
-                       dim3(p.H, p.B), dim3(C::NT), 0, stream, p);
+    launch_kernel((kda_verify_grid_kernel<D, QMAX, ACT_BF16, false>),
+                  dim3(p.H, p.B), dim3(C::NT), 0, stream, p);
     return int(hipGetLastError());
   }
   // Tickets (also for more requests than a grid row holds).
@@ -1265,7 +1265,7 @@ int launch_one(const VerifyParams& p, int schedule, int grid,
   if (q.per_ticket <= 0) q.per_ticket = 1;
   q.n_tickets = (q.n_items + q.per_ticket - 1) / q.per_ticket;
   grid = min(grid, q.n_tickets);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, stream, q);
+  launch_kernel(kern, dim3(grid), dim3(C::NT), 0, stream, q);
   return int(hipGetLastError());
 }
 

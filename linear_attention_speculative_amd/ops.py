@@ -184,6 +184,27 @@ def reset_counter(counter: torch.Tensor, stream=None) -> None:
         _raise(rc)
 
 
+def set_launch_events(start=None, stop=None, launches: int = 1) -> int:
+    """Time the next `launches` kernels that library calls on this thread
+    launch: `start` (a torch.cuda.Event, created by one record beforehand,
+    or None) records the start of the first, `stop` the end of the last,
+    from the kernels' own dispatch (kda_set_launch_events).  Returns how
+    many launches the previous arming was still waiting for."""
+    def handle(ev):
+        if ev is None:
+            return None
+        h = ev.cuda_event
+        if not h:
+            raise ValueError("record the event once before arming it")
+        return h
+    left = ctypes.c_int32(0)
+    rc = _abi.load().kda_set_launch_events(handle(start), handle(stop),
+                                           int(launches), ctypes.byref(left))
+    if rc != _abi.KDA_OK:
+        _raise(rc)
+    return left.value
+
+
 def abi_version() -> int:
     return _abi.load().kda_abi_version()
 

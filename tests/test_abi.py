@@ -31,8 +31,27 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_abi.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert kda.abi_version() == 5
+    assert kda.abi_version() == 6
     assert lib.kda_status_string(_abi.KDA_E_UNALIGNED) == b"KDA_E_UNALIGNED"
+
+
+def test_launch_events_arming_is_checked():
+    """Arming the kernel timing takes launches >= 0; 0 (or NULL events)
+    arms nothing, a negative count is an argument error."""
+    lib = _abi.load()
+    left = ctypes.c_int32(-1)
+    assert lib.kda_set_launch_events(None, None, 0, None) == _abi.KDA_OK
+    assert lib.kda_set_launch_events(None, None, 3, None) == _abi.KDA_OK
+    assert lib.kda_set_launch_events(None, None, -1,
+                                     ctypes.byref(left)) == _abi.KDA_E_ARG
+    assert b"launches" in lib.kda_last_error()
+    assert left.value == -1                  # untouched on error
+    assert lib.kda_set_launch_events(None, None, 0,
+                                     ctypes.byref(left)) == _abi.KDA_OK
+    assert left.value == 3                   # none of the 3 happened
+    assert lib.kda_set_launch_events(None, None, 0,
+                                     ctypes.byref(left)) == _abi.KDA_OK
+    assert left.value == 0
 
 
 def _kw(**over):
