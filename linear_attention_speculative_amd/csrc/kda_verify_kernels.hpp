@@ -82,13 +82,20 @@ struct VerifyCfg {
   static constexpr int NN = QMAX * (QMAX + 1) / 2;  // <k_s, P q_t>, s <= t
   static constexpr int NV = 2 * QMAX + NM + NN;     // reduced scalars
   static constexpr int DS = 2 * QMAX + 4;           // padded row of dots
-  // LDS reduction tree: columns are summed in chunks of CH, NB scalars at
-  // a time (the whole set when it fits in 20 KiB: at Q = 8 that keeps the
-  // workgroup under 40 KiB of LDS, so four of them fit on a CU).
+  // Column sums, D >= 64 and Q <= 8: each wave reduces its group's NS
+  // scalars over its 64 columns with a transposing lane reduction (16
+  // scalars at a time), one LDS word per scalar and wave, one barrier.
+  // Otherwise an LDS reduction tree: columns summed in chunks of CH, NB
+  // scalars at a time (at Q = 16 the 144 scalars of a group, each a product
+  // of up to 15 decays, would not fit the registers).
+  static constexpr bool WAVE_COLS = D >= 64 && QMAX <= 8;
+  static constexpr int WPG = WAVE_COLS ? D / 64 : 1;  // waves per group
+  static constexpr int NS = (NV + NG - 1) / NG;       // scalars per group
   static constexpr int CH = D >= 32 ? 32 : D;
   static constexpr int NCH = D / CH;
   static constexpr int NB = NV * D <= 5120 ? NV : 5120 / D;
-  static constexpr int PART = NB * D > D * DS ? NB * D : D * DS;
+  static constexpr int PART =
+      WAVE_COLS ? D * DS : (NB * D > D * DS ? NB * D : D * DS);
   // conv channels: q and k of the whole head, v of this workgroup's rows
   static constexpr int NCONV = 2 * D + DV;
   static constexpr int JC = (NCONV + NT - 1) / NT;  // conv channels/thread
@@ -116,10 +123,12 @@ struct alignas(16) VerifySmem {
   __device__ float (*vec())[D] {
     return reinterpret_cast<float (*)[D]>(&y[0][0][0]);
   }
-  // column partial sums [NB][D] (phase 1), then per row:
+  // column partial sums [NB][D] (phase 1, D < 64), then per row:
   // S.(Gam k_hat_t), S.(Gam q_hat_t) [D][DS] (phases 3-4)
   float part[C::PART];
-  float red[C::NV * C::NCH];     // chunk sums of the column partials
+  // column sums: per wave and scalar of its group (D >= 64), else chunk
+  // sums of the column partials
+  float red[C::WAVE_COLS ? (C::NT_HEAD / 64) * C::NV : C::NV * C::NCH];
   float Mc[QMAX][QMAX];          // <k_hat_s, P_{s,t} k_hat_t>, s < t
   float Nc[QMAX][QMAX];          // <k_hat_s, P_{s,t} q_hat_t>, s <= t
   float beta[QMAX];
@@ -511,6 +520,70 @@ __device__ __forceinline__ void item_front(
   if (tid < q) sm.beta[tid] = sigmoidf_(A::f(s.bv));
 }
 
+// ---- column sums by lane reduction (D >= 64) ---------------------------------
+// Scalar IDX of the reduction vector for this thread's column: |k_t|^2,
+// |q_t|^2, then <k_s, P_{s,t} k_t> (s < t) and <k_s, P_{s,t} q_t> (s <= t),
+// P_{s,t} = d_{s+1} ... d_t multiplied up from s + 1; IDX >= NV is 0.
+template <int QMAX, int IDX>
+__device__ __forceinline__ float column_scalar(const float (&kk)[QMAX],
+                                              const float (&qq)[QMAX],
+                                              const float (&dd)[QMAX]) {
+  constexpr int NM = QMAX * (QMAX - 1) / 2;
+  constexpr int NV = 2 * QMAX + NM + QMAX * (QMAX + 1) / 2;
+  if constexpr (IDX >= NV) {
+    return 0.0f;
+  } else if constexpr (IDX < QMAX) {
+    return kk[IDX] * kk[IDX];
+  } else if constexpr (IDX < 2 * QMAX) {
+    return qq[IDX - QMAX] * qq[IDX - QMAX];
+  } else {
+    constexpr bool M = IDX < 2 * QMAX + NM;
+    constexpr int R = M ? IDX - 2 * QMAX : IDX - 2 * QMAX - NM;
+    // R = t (t - 1) / 2 + s (M) or t (t + 1) / 2 + s
+    constexpr int T = [] {
+      int t = 0;
+      while ((M ? (t + 1) * t / 2 : (t + 1) * (t + 2) / 2) <= R) ++t;
+      return t;
+    }();
+    constexpr int S = R - (M ? T * (T - 1) / 2 : T * (T + 1) / 2);
+    float P = 1.0f;
+#pragma unroll
+    for (int r = S + 1; r <= T; ++r) P *= dd[r];
+    return M ? kk[S] * P * kk[T] : kk[S] * P * qq[T];
+  }
+}
+
+// One 16-scalar chunk of group G (scalars G, G + NG, G + 2 NG, ...):
+// transposing reduction over each 16-lane row, then across the rows, and
+// lane j < 16 stores the wave's sum of the chunk's scalar j.
+template <int QMAX, int G, int NG, int NS, int K, size_t... I>
+__device__ __forceinline__ void column_chunk(const float (&kk)[QMAX],
+                                             const float (&qq)[QMAX],
+                                             const float (&dd)[QMAX],
+                                             float* dst, int lane,
+                                             std::index_sequence<I...>) {
+  float v[16] = {column_scalar<QMAX, G + (K * 16 + int(I)) * NG>(kk, qq,
+                                                                  dd)...};
+  float r = transpose_sum<16, 16>(v, lane);
+  r += __int_as_float(
+      __builtin_amdgcn_ds_swizzle(__float_as_int(r), 0x401F));  // xor 16
+  r += __int_as_float(
+      __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(r)));
+  const int pos = K * 16 + (lane & 15);
+  if (lane < 16 && pos < NS) dst[pos] = r;
+}
+
+template <int QMAX, int G, int NG, int NS, size_t... K>
+__device__ __forceinline__ void column_group(const float (&kk)[QMAX],
+                                             const float (&qq)[QMAX],
+                                             const float (&dd)[QMAX],
+                                             float* dst, int lane,
+                                             std::index_sequence<K...>) {
+  (column_chunk<QMAX, G, NG, NS, int(K)>(kk, qq, dd, dst, lane,
+                                         std::make_index_sequence<16>{}),
+   ...);
+}
+
 // Phases 1-4 of a live item (after the barrier that publishes phase 0),
 // with its state tile (rows v0 .. v0 + DV) in registers.
 template <int D, int QMAX, bool FULL, int DV = D, class PreDots>
@@ -527,7 +600,7 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
   const int lg = tid % C::L;      // lane within its row group
   const int rg = tid / C::L;      // row group
 
-  // ---- phase 1: per-column partial sums, summed over columns in LDS ---------
+  // ---- phase 1: per-column partial sums, summed over the columns ------------
   const int col = tid % D;
   const int grp = C::NG > 1 ? tid / D : 0;          // column group
   const bool col_ok = tid < D || C::NG > 1;
@@ -539,59 +612,80 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
     qq[t] = ok ? sm.y[0][t][col] : 0.0f;
     dd[t] = ok ? sm.dec[t][col] : 1.0f;
   }
+  if constexpr (C::WAVE_COLS) {
+    // wave w sums the scalars of group w / WPG over its 64 columns
+    const int lane = tid & 63;
+    float* dst = &sm.red[(tid >> 6) * C::NS];
+    constexpr int NK = (C::NS + 15) / 16;
+    if (C::NG == 1 || grp == 0)
+      column_group<QMAX, 0, C::NG, C::NS>(kk, qq, dd, dst, lane,
+                                          std::make_index_sequence<NK>{});
+    else
+      column_group<QMAX, 1, C::NG, C::NS>(kk, qq, dd, dst, lane,
+                                          std::make_index_sequence<NK>{});
+    lds_barrier();
+  } else {
 #pragma unroll
-  for (int v0 = 0; v0 < C::NV; v0 += C::NB) {
-    // With several batches, each batch recomputes its products: opaque
-    // copies of the inputs keep the compiler from carrying shared partial
-    // products across the barrier in extra registers.
-    if constexpr (C::NV > C::NB) {
+    for (int v0 = 0; v0 < C::NV; v0 += C::NB) {
+      // With several batches, each batch recomputes its products: opaque
+      // copies of the inputs keep the compiler from carrying shared partial
+      // products across the barrier in extra registers.
+      if constexpr (C::NV > C::NB) {
 #pragma unroll
-      for (int t = 0; t < QMAX; ++t)
-        asm volatile("" : "+v"(kk[t]), "+v"(qq[t]), "+v"(dd[t]));
-    }
-    // this thread's share of scalars [v0, v0 + NB)
-    auto put = [&](int idx, float val) {
-      if (idx >= v0 && idx < v0 + C::NB && idx % C::NG == grp && col_ok)
-        sm.part[(idx - v0) * D + col] = val;
-    };
+        for (int t = 0; t < QMAX; ++t)
+          asm volatile("" : "+v"(kk[t]), "+v"(qq[t]), "+v"(dd[t]));
+      }
+      // this thread's share of scalars [v0, v0 + NB)
+      auto put = [&](int idx, float val) {
+        if (idx >= v0 && idx < v0 + C::NB && idx % C::NG == grp && col_ok)
+          sm.part[(idx - v0) * D + col] = val;
+      };
 #pragma unroll
-    for (int t = 0; t < QMAX; ++t) {
-      put(t, kk[t] * kk[t]);
-      put(QMAX + t, qq[t] * qq[t]);
-    }
+      for (int t = 0; t < QMAX; ++t) {
+        put(t, kk[t] * kk[t]);
+        put(QMAX + t, qq[t] * qq[t]);
+      }
 #pragma unroll
-    for (int s = 0; s < QMAX; ++s) {
-      float P = 1.0f;
+      for (int s = 0; s < QMAX; ++s) {
+        float P = 1.0f;
 #pragma unroll
-      for (int t = s; t < QMAX; ++t) {
-        if (t > s) {
-          P *= dd[t];
-          put(idx_m<QMAX>(t, s), kk[s] * P * kk[t]);
+        for (int t = s; t < QMAX; ++t) {
+          if (t > s) {
+            P *= dd[t];
+            put(idx_m<QMAX>(t, s), kk[s] * P * kk[t]);
+          }
+          put(idx_n<QMAX>(t, s), kk[s] * P * qq[t]);
         }
-        put(idx_n<QMAX>(t, s), kk[s] * P * qq[t]);
       }
-    }
-    lds_barrier();
-    // chunk sums: scalar v, columns [c*CH, (c+1)*CH)
-    for (int task = tid; task < C::NB * C::NCH; task += C::NT) {
-      const int v = task / C::NCH, c = task - v * C::NCH;
-      if (v0 + v < C::NV) {
-        const f4* src =
-            reinterpret_cast<const f4*>(&sm.part[v * D + c * C::CH]);
-        f4 acc = src[0];
+      lds_barrier();
+      // chunk sums: scalar v, columns [c*CH, (c+1)*CH)
+      for (int task = tid; task < C::NB * C::NCH; task += C::NT) {
+        const int v = task / C::NCH, c = task - v * C::NCH;
+        if (v0 + v < C::NV) {
+          const f4* src =
+              reinterpret_cast<const f4*>(&sm.part[v * D + c * C::CH]);
+          f4 acc = src[0];
 #pragma unroll
-        for (int i = 1; i < C::CH / 4; ++i) acc += src[i];
-        sm.red[(v0 + v) * C::NCH + c] = (acc.x + acc.y) + (acc.z + acc.w);
+          for (int i = 1; i < C::CH / 4; ++i) acc += src[i];
+          sm.red[(v0 + v) * C::NCH + c] = (acc.x + acc.y) + (acc.z + acc.w);
+        }
       }
+      lds_barrier();
     }
-    lds_barrier();
   }
 
   // ---- phase 2: norms, column vectors, coefficient matrices ------------------
   auto total = [&](int idx) {
     float s = 0.0f;
+    if constexpr (C::WAVE_COLS) {
+      const int g = idx % C::NG, pos = idx / C::NG;
 #pragma unroll
-    for (int c = 0; c < C::NCH; ++c) s += sm.red[idx * C::NCH + c];
+      for (int w = 0; w < C::WPG; ++w)
+        s += sm.red[(g * C::WPG + w) * C::NS + pos];
+    } else {
+#pragma unroll
+      for (int c = 0; c < C::NCH; ++c) s += sm.red[idx * C::NCH + c];
+    }
     return s;
   };
   const float inv_sqrt_d = 1.0f / sqrtf(float(D));
