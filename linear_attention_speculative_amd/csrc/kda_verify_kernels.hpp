@@ -131,6 +131,11 @@ struct alignas(16) VerifySmem {
   float red[C::WAVE_COLS ? (C::NT_HEAD / 64) * C::NV : C::NV * C::NCH];
   float Mc[QMAX][QMAX];          // <k_hat_s, P_{s,t} k_hat_t>, s < t
   float Nc[QMAX][QMAX];          // <k_hat_s, P_{s,t} q_hat_t>, s <= t
+  // column sums by lane reduction: the unnormalised column vectors
+  // Gam_t k_t, Gam_t q_t (written in phase 1) and the norm factors that
+  // phase 4 applies to the row sums
+  float uvec[C::WAVE_COLS ? 2 * QMAX : 1][D];
+  float nrm[2][QMAX];
   float beta[QMAX];
   int ticket[2];
 };
@@ -617,6 +622,19 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
     const int lane = tid & 63;
     float* dst = &sm.red[(tid >> 6) * C::NS];
     constexpr int NK = (C::NS + 15) / 16;
+    // The column vectors need no norm: the dot products take Gam_t k_t and
+    // Gam_t q_t, and phase 4 scales each row sum by the norm factor of its
+    // position, so phase 3 starts one barrier earlier.  (Written before the
+    // reduction, which then holds only its own values.)
+    if (tid < D) {
+      float gam = 1.0f;
+#pragma unroll
+      for (int t = 0; t < QMAX; ++t) {
+        gam *= dd[t];
+        sm.uvec[t][tid] = gam * kk[t];
+        sm.uvec[QMAX + t][tid] = gam * qq[t];
+      }
+    }
     if (C::NG == 1 || grp == 0)
       column_group<QMAX, 0, C::NG, C::NS>(kk, qq, dd, dst, lane,
                                           std::make_index_sequence<NK>{});
@@ -689,7 +707,26 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
     return s;
   };
   const float inv_sqrt_d = 1.0f / sqrtf(float(D));
-  if (tid < D) {
+  if constexpr (C::WAVE_COLS) {
+    // coefficient matrices and norm factors, published to phase 4 by the
+    // barrier after phase 3
+    for (int j = tid; j < QMAX * QMAX + QMAX; j += C::NT) {
+      if (j < QMAX * QMAX) {
+        const int t = j / QMAX, s = j - t * QMAX;
+        const float rks = rsqrtf(total(s) + kNormEps);
+        const float rkt = rsqrtf(total(t) + kNormEps);
+        const float rqt = rsqrtf(total(QMAX + t) + kNormEps) * inv_sqrt_d;
+        sm.Mc[t][s] = s < t ? total(idx_m<QMAX>(t, s)) * rks * rkt : 0.0f;
+        sm.Nc[t][s] = s <= t ? total(idx_n<QMAX>(t, s)) * rks * rqt : 0.0f;
+      } else {
+        const int t = j - QMAX * QMAX;
+        sm.nrm[0][t] = rsqrtf(total(t) + kNormEps);
+        sm.nrm[1][t] = rsqrtf(total(QMAX + t) + kNormEps) * inv_sqrt_d;
+      }
+    }
+    // keep phase 3's loads from being scheduled into this (registers)
+    __builtin_amdgcn_sched_barrier(0);
+  } else if (tid < D) {
     // q, k and the decays are read again here (thread tid's own column),
     // so that they need not stay in registers across phase 1's barriers
     float gam = 1.0f;
@@ -705,15 +742,17 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
       sm.vec()[QMAX + t][tid] = gam * qt * rq;
     }
   }
-  for (int j = tid; j < QMAX * QMAX; j += C::NT) {
-    const int t = j / QMAX, s = j - t * QMAX;
-    const float rks = rsqrtf(total(s) + kNormEps);
-    const float rkt = rsqrtf(total(t) + kNormEps);
-    const float rqt = rsqrtf(total(QMAX + t) + kNormEps) * inv_sqrt_d;
-    sm.Mc[t][s] = s < t ? total(idx_m<QMAX>(t, s)) * rks * rkt : 0.0f;
-    sm.Nc[t][s] = s <= t ? total(idx_n<QMAX>(t, s)) * rks * rqt : 0.0f;
+  if constexpr (!C::WAVE_COLS) {
+    for (int j = tid; j < QMAX * QMAX; j += C::NT) {
+      const int t = j / QMAX, s = j - t * QMAX;
+      const float rks = rsqrtf(total(s) + kNormEps);
+      const float rkt = rsqrtf(total(t) + kNormEps);
+      const float rqt = rsqrtf(total(QMAX + t) + kNormEps) * inv_sqrt_d;
+      sm.Mc[t][s] = s < t ? total(idx_m<QMAX>(t, s)) * rks * rkt : 0.0f;
+      sm.Nc[t][s] = s <= t ? total(idx_n<QMAX>(t, s)) * rks * rqt : 0.0f;
+    }
+    lds_barrier();
   }
-  lds_barrier();
 
   // (the deferred flush folds the pending positions into the tile here)
   pre_dots(st);
@@ -743,7 +782,8 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
 #pragma unroll
         for (int c = 0; c < C::CHUNKS; ++c)
           va[c] = *reinterpret_cast<const f4*>(
-              &sm.vec()[w * QMAX + t][c * 4 * C::L + 4 * lg]);
+              C::WAVE_COLS ? &sm.uvec[w * QMAX + t][c * 4 * C::L + 4 * lg]
+                           : &sm.vec()[w * QMAX + t][c * 4 * C::L + 4 * lg]);
 #pragma unroll
         for (int pp = 0; pp < C::PASSES; ++pp) {
           float sa = 0.0f;
@@ -778,11 +818,12 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
 #pragma unroll
     for (int t = 0; t < QMAX; ++t) {
       if (t < q) {
-        float u = drow[t];
+        float u = C::WAVE_COLS ? drow[t] * sm.nrm[0][t] : drow[t];
 #pragma unroll
         for (int s = 0; s < t; ++s) u = fmaf(sm.Mc[t][s], cc[s], u);
         cc[t] = sm.beta[t] * (sm.y[2][t][v] - u);
-        float o = drow[QMAX + t];
+        float o = C::WAVE_COLS ? drow[QMAX + t] * sm.nrm[1][t]
+                               : drow[QMAX + t];
 #pragma unroll
         for (int s = 0; s <= t; ++s) o = fmaf(sm.Nc[t][s], cc[s], o);
         if (p.flags & kOutBf16)
