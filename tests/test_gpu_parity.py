@@ -234,6 +234,21 @@ def test_edge_cases_verify_and_commit():
     _commit_case(wl, {0: (sample, ref)}, lens=lens_c)
 
 
+def test_batch_beyond_one_grid_row():
+    """65,636 requests, more than one grid row of 65,535 holds: the default
+    schedule takes the ticket kernel and the commit its strided kernel. The
+    requests on both sides of 65,535 and the last ones match the oracle, and
+    every slot no request names is unchanged."""
+    B = 65536 + 100
+    wl = make_workload("ragged", DEV, B=B, H=1, D=16, Q=2, N=B + 64,
+                       null_frac=0.05)
+    reqs = (list(range(0, 8)) + list(range(65528, 65544)) +
+            list(range(B - 8, B)))
+    sample, ref, errs = _verify_case(wl, reqs=reqs)
+    cerr = _commit_case(wl, {0: (sample, ref)})
+    print("beyond one grid row", errs, cerr)
+
+
 def test_commit_to_final_slots():
     wl = make_workload("ragged", DEV, B=6, H=2, D=64, Q=4, N=20,
                        null_frac=0.0)
