@@ -82,20 +82,22 @@ struct VerifyCfg {
   static constexpr int NN = QMAX * (QMAX + 1) / 2;  // <k_s, P q_t>, s <= t
   static constexpr int NV = 2 * QMAX + NM + NN;     // reduced scalars
   static constexpr int DS = 2 * QMAX + 4;           // padded row of dots
-  // Column sums, D >= 64 and Q <= 8: each wave reduces its group's NS
-  // scalars over its 64 columns with a transposing lane reduction (16
-  // scalars at a time), one LDS word per scalar and wave, one barrier.
-  // Otherwise an LDS reduction tree: columns summed in chunks of CH, NB
-  // scalars at a time (at Q = 16 the 144 scalars of a group, each a product
-  // of up to 15 decays, would not fit the registers).
-  static constexpr bool WAVE_COLS = D >= 64 && QMAX <= 8;
+  // Column sums, D >= 64: each wave reduces its group's NS scalars over its
+  // 64 columns with a transposing lane reduction (16 scalars at a time),
+  // one LDS word per scalar and wave, one barrier.  Otherwise an LDS
+  // reduction tree: columns summed in chunks of CH, NB scalars at a time
+  // (NV / NB batches of two barriers each: eight at Q = 16, where they took
+  // 28 of an item's 48 us).  The ticket loop keeps the tree at Q = 16: the
+  // lane reduction's 144 scalars per group would spill its registers.
+  static constexpr bool WAVE_COLS = D >= 64;
+  static constexpr bool TREE = !WAVE_COLS || QMAX > 8;  // tree space needed
   static constexpr int WPG = WAVE_COLS ? D / 64 : 1;  // waves per group
   static constexpr int NS = (NV + NG - 1) / NG;       // scalars per group
   static constexpr int CH = D >= 32 ? 32 : D;
   static constexpr int NCH = D / CH;
   static constexpr int NB = NV * D <= 5120 ? NV : 5120 / D;
   static constexpr int PART =
-      WAVE_COLS ? D * DS : (NB * D > D * DS ? NB * D : D * DS);
+      TREE ? (NB * D > D * DS ? NB * D : D * DS) : D * DS;
   // conv channels: q and k of the whole head, v of this workgroup's rows
   static constexpr int NCONV = 2 * D + DV;
   static constexpr int JC = (NCONV + NT - 1) / NT;  // conv channels/thread
@@ -128,7 +130,9 @@ struct alignas(16) VerifySmem {
   float part[C::PART];
   // column sums: per wave and scalar of its group (D >= 64), else chunk
   // sums of the column partials
-  float red[C::WAVE_COLS ? (C::NT_HEAD / 64) * C::NV : C::NV * C::NCH];
+  float red[C::WAVE_COLS && (C::NT_HEAD / 64) * C::NV > C::NV * C::NCH
+                ? (C::NT_HEAD / 64) * C::NV
+                : C::NV * C::NCH];
   float Mc[QMAX][QMAX];          // <k_hat_s, P_{s,t} k_hat_t>, s < t
   float Nc[QMAX][QMAX];          // <k_hat_s, P_{s,t} q_hat_t>, s <= t
   // column sums by lane reduction: the unnormalised column vectors
@@ -591,13 +595,17 @@ __device__ __forceinline__ void column_group(const float (&kk)[QMAX],
 
 // Phases 1-4 of a live item (after the barrier that publishes phase 0),
 // with its state tile (rows v0 .. v0 + DV) in registers.
-template <int D, int QMAX, bool FULL, int DV = D, class PreDots>
+// PERSISTENT: the ticket loop (keeps the LDS tree at Q = 16).
+template <int D, int QMAX, bool FULL, int DV = D, bool PERSISTENT = false,
+          class PreDots>
 __device__ __forceinline__ void item_back(const VerifyParams& p,
                                           VerifySmem<D, QMAX>& sm,
                                           const Item& it,
                                           Tile<D, QMAX, DV>& st,
                                           PreDots&& pre_dots) {
   using C = VerifyCfg<D, QMAX, DV>;
+  // column sums by lane reduction (else the LDS tree)
+  constexpr bool LANES = C::WAVE_COLS && (QMAX <= 8 || !PERSISTENT);
   const int tid = fresh_tid();
   const int h = it.h;
   const int q = FULL ? QMAX : it.q;
@@ -617,7 +625,7 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
     qq[t] = ok ? sm.y[0][t][col] : 0.0f;
     dd[t] = ok ? sm.dec[t][col] : 1.0f;
   }
-  if constexpr (C::WAVE_COLS) {
+  if constexpr (LANES) {
     // wave w sums the scalars of group w / WPG over its 64 columns
     const int lane = tid & 63;
     float* dst = &sm.red[(tid >> 6) * C::NS];
@@ -695,7 +703,7 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
   // ---- phase 2: norms, column vectors, coefficient matrices ------------------
   auto total = [&](int idx) {
     float s = 0.0f;
-    if constexpr (C::WAVE_COLS) {
+    if constexpr (LANES) {
       const int g = idx % C::NG, pos = idx / C::NG;
 #pragma unroll
       for (int w = 0; w < C::WPG; ++w)
@@ -707,7 +715,7 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
     return s;
   };
   const float inv_sqrt_d = 1.0f / sqrtf(float(D));
-  if constexpr (C::WAVE_COLS) {
+  if constexpr (LANES) {
     // coefficient matrices and norm factors, published to phase 4 by the
     // barrier after phase 3
     for (int j = tid; j < QMAX * QMAX + QMAX; j += C::NT) {
@@ -742,7 +750,7 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
       sm.vec()[QMAX + t][tid] = gam * qt * rq;
     }
   }
-  if constexpr (!C::WAVE_COLS) {
+  if constexpr (!LANES) {
     for (int j = tid; j < QMAX * QMAX; j += C::NT) {
       const int t = j / QMAX, s = j - t * QMAX;
       const float rks = rsqrtf(total(s) + kNormEps);
@@ -782,7 +790,7 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
 #pragma unroll
         for (int c = 0; c < C::CHUNKS; ++c)
           va[c] = *reinterpret_cast<const f4*>(
-              C::WAVE_COLS ? &sm.uvec[w * QMAX + t][c * 4 * C::L + 4 * lg]
+              LANES ? &sm.uvec[w * QMAX + t][c * 4 * C::L + 4 * lg]
                            : &sm.vec()[w * QMAX + t][c * 4 * C::L + 4 * lg]);
 #pragma unroll
         for (int pp = 0; pp < C::PASSES; ++pp) {
@@ -818,11 +826,11 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
 #pragma unroll
     for (int t = 0; t < QMAX; ++t) {
       if (t < q) {
-        float u = C::WAVE_COLS ? drow[t] * sm.nrm[0][t] : drow[t];
+        float u = LANES ? drow[t] * sm.nrm[0][t] : drow[t];
 #pragma unroll
         for (int s = 0; s < t; ++s) u = fmaf(sm.Mc[t][s], cc[s], u);
         cc[t] = sm.beta[t] * (sm.y[2][t][v] - u);
-        float o = C::WAVE_COLS ? drow[QMAX + t] * sm.nrm[1][t]
+        float o = LANES ? drow[QMAX + t] * sm.nrm[1][t]
                                : drow[QMAX + t];
 #pragma unroll
         for (int s = 0; s <= t; ++s) o = fmaf(sm.Nc[t][s], cc[s], o);
@@ -1134,7 +1142,8 @@ __device__ __forceinline__ void verify_item(const VerifyParams& p,
   lds_barrier();
   // Metadata of the next item: scalar loads in flight from here on.
   advance();
-  item_back<D, QMAX, FULL, DV>(p, sm, it, st, [&](Tile<D, QMAX, DV>& t) {
+  item_back<D, QMAX, FULL, DV, PERSISTENT>(p, sm, it, st,
+                                           [&](Tile<D, QMAX, DV>& t) {
     if constexpr (FLUSH) {
       if (n_pend > 0) flush_fold<D, QMAX>(p, fs, it, n_pend, t);
     }
