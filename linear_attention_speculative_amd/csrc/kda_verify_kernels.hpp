@@ -956,27 +956,33 @@ __device__ __forceinline__ void flush_fold(const VerifyParams& p,
   const int lg = tid % C::L, rg = tid / C::L;
   float* dst = const_cast<float*>(p.state) + int64_t(it.slot) * p.s_slot +
                int64_t(it.h) * D * D;
+  // Column chunk outer, position inner, the tile updated in place: one
+  // column vector and one correction per pass are live at a time (the
+  // operations per element are the same, in the same order).
 #pragma unroll
-  for (int pp = 0; pp < C::PASSES; ++pp) {
-    const int row = pp * C::RPP + rg;
+  for (int c = 0; c < C::CHUNKS; ++c) {
+    const int col = c * 4 * C::L + 4 * lg;
+    const f4 g4 = *reinterpret_cast<const f4*>(&fs.gam[col]);
 #pragma unroll
-    for (int c = 0; c < C::CHUNKS; ++c) {
-      const int col = c * 4 * C::L + 4 * lg;
-      f4 acc = st[pp][c] * *reinterpret_cast<const f4*>(&fs.gam[col]);
+    for (int pp = 0; pp < C::PASSES; ++pp) st[pp][c] = st[pp][c] * g4;
 #pragma unroll
-      for (int t = 0; t < QMAX; ++t) {
-        if (t < n) {
-          const float cv = fs.cT[row][t];
-          const f4 w4 = *reinterpret_cast<const f4*>(&fs.w[t][col]);
-          acc.x = fmaf(cv, w4.x, acc.x);
-          acc.y = fmaf(cv, w4.y, acc.y);
-          acc.z = fmaf(cv, w4.z, acc.z);
-          acc.w = fmaf(cv, w4.w, acc.w);
+    for (int t = 0; t < QMAX; ++t) {
+      if (t < n) {
+        const f4 w4 = *reinterpret_cast<const f4*>(&fs.w[t][col]);
+#pragma unroll
+        for (int pp = 0; pp < C::PASSES; ++pp) {
+          const float cv = fs.cT[pp * C::RPP + rg][t];
+          f4& a = st[pp][c];
+          a.x = fmaf(cv, w4.x, a.x);
+          a.y = fmaf(cv, w4.y, a.y);
+          a.z = fmaf(cv, w4.z, a.z);
+          a.w = fmaf(cv, w4.w, a.w);
         }
       }
-      st[pp][c] = acc;
-      st_stream(dst + row * D + col, acc);
     }
+#pragma unroll
+    for (int pp = 0; pp < C::PASSES; ++pp)
+      st_stream(dst + (pp * C::RPP + rg) * D + col, st[pp][c]);
   }
 }
 
