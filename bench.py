@@ -23,9 +23,10 @@ stream between two launches adds its marker's gap, 6-11 us here, to the
 kernel it brackets), over K more eager steps; `kernels` gives each kernel's
 median, p10 and p90 over those steps, the median of single synchronized
 launches, and the
-median of single launches that each follow an untimed 1 GiB write (which
-evicts the caches), so that any help from the last-level cache between
-kernels shows up as a difference; `cpu_baseline`
+median of single launches that each follow an untimed write and read of a
+1 GiB buffer (which evicts the caches and leaves no dirty lines for the
+timed kernel to write back), so that any help from the last-level cache
+between kernels shows up as a difference; `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload;
 `step_hbm.frac_of_copy` relates the step's bandwidth to a plain 1 GiB
 device copy timed in the same run; `deferred_form` (headline only) times
@@ -54,11 +55,11 @@ Other workloads (`--workload`), each one JSON line of the same form:
   ragged    64 requests with ragged windows (q uniform in 1..4) and 10%
             null slots, verify only; its state (about 116 MiB) fits the
             256 MB last-level cache, so every timed launch follows an
-            untimed 1 GiB write that evicts it.
+            untimed 1 GiB write and read that evicts it.
 The default run (headline) is the one the throughput figure is quoted on.
-`--cold-steps` times any workload that way (an evicting write before every
-timed step, the step timed from its first kernel's start to its last
-kernel's end).
+`--cold-steps` times any workload that way (an evicting write and read
+before every timed step, the step timed from its first kernel's start to
+its last kernel's end).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold-steps]
   python bench.py --copy-calibration   # plain copy for HBM counter scaling
@@ -78,7 +79,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 METRIC = ("verified tokens/s + % HBM peak (KDA verify+commit, H=32 K=V=128, "
           "Q=4)")
-EVICT_BYTES = 1 << 30          # the cache-evicting write before cold steps
+EVICT_BYTES = 1 << 30          # the cache-evicting buffer before cold steps
+
+
+def evict_caches(buf, k: float) -> None:
+    """Untimed: write the 1 GiB buffer, then read it back.  The write alone
+    would evict the caches but leave up to 256 MB of dirty last-level-cache
+    lines, which the next (timed) kernel would then write back to HBM
+    (measured: 148 us for a 127 us verify); the read leaves clean lines."""
+    buf.fill_(k)
+    buf.sum()
 # workloads whose every timed launch is cold (the state fits the caches)
 COLD_WORKLOADS = ("ragged",)
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -365,7 +375,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle sample (0: skip)")
     ap.add_argument("--cold", type=int, default=10,
-                    help="launches timed after a cache-evicting write")
+                    help="launches timed after a cache-evicting write and "
+                         "read")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time the K steps as eager launches, not as one "
@@ -377,8 +388,9 @@ def main() -> int:
                          "v-tiles (0: the library's choice)")
     ap.add_argument("--cold-steps", action="store_true",
                     help="precede every timed step with an untimed 1 GiB "
-                         "write that evicts the caches; the step time is "
-                         "then taken from events around its launches")
+                         "write and read that evict the caches; the step "
+                         "time is then taken from events around its "
+                         "launches")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -446,7 +458,7 @@ def main() -> int:
     t0 = time.perf_counter()
     for k in range(args.steps):
         if evict is not None:
-            evict.fill_(float(k))          # untimed: before the first kernel
+            evict_caches(evict, float(k))  # untimed: before the first kernel
             step(events[k])
         else:
             step()
@@ -505,8 +517,8 @@ def main() -> int:
     def quant(xs, q):
         return xs[min(len(xs) - 1, int(q * len(xs)))]
 
-    # Cold phases: each after an untimed 1 GiB write; then the same single
-    # phases without the write.  The difference to the back-to-back steps
+    # Cold phases: each after an untimed 1 GiB write and read; then the same
+    # single phases without it.  The difference to the back-to-back steps
     # is launch ramp-up and drain, the difference between the two is what
     # the caches kept between kernels.
     scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -524,7 +536,7 @@ def main() -> int:
 
     for k in range(args.cold):
         for i, (_, _, n, fn) in enumerate(phases):
-            scratch.fill_(float(k) + 0.5 * i)
+            evict_caches(scratch, float(k) + 0.5 * i)
             cold[i].append(timed(fn, n))
     del scratch
     for k in range(args.cold):
@@ -588,7 +600,7 @@ def main() -> int:
                      "kernel": kname, "bytes_per_launch": by,
                      "us_per_launch": ms * 1e3,
                      # the same kernel launched after an untimed 1 GiB
-                     # write that evicts the caches (median of --cold)
+                     # write and read that evict the caches (median of --cold)
                      "cold": None if not cold[dom] else {
                          "us_per_launch": quant(cold[dom], 0.5),
                          "achieved": by / (quant(cold[dom], 0.5) * 1e-6)
