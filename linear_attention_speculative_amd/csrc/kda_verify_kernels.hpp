@@ -127,7 +127,7 @@ struct alignas(16) VerifySmem {
   }
   // column partial sums [NB][D] (phase 1, D < 64), then per row:
   // S.(Gam k_hat_t), S.(Gam q_hat_t) [D][DS] (phases 3-4)
-  float part[C::PART];
+  alignas(16) float part[C::PART];  // (read as float4)
   // column sums: per wave and scalar of its group (D >= 64), else chunk
   // sums of the column partials
   float red[C::WAVE_COLS && (C::NT_HEAD / 64) * C::NV > C::NV * C::NCH
@@ -138,7 +138,7 @@ struct alignas(16) VerifySmem {
   // column sums by lane reduction: the unnormalised column vectors
   // Gam_t k_t, Gam_t q_t (written in phase 1) and the norm factors that
   // phase 4 applies to the row sums
-  float uvec[C::WAVE_COLS ? 2 * QMAX : 1][D];
+  alignas(16) float uvec[C::WAVE_COLS ? 2 * QMAX : 1][D];  // (float4)
   float nrm[2][QMAX];
   float beta[QMAX];
   int ticket[2];

@@ -44,20 +44,21 @@ def _raise(code: int):
     raise cls(code, msg)
 
 
+_DIMS4 = ctypes.c_int64 * 4
+_PAD = ((0, 0, 0, 0), (0, 0, 0), (0, 0), (0,), ())
+
+
 def describe(t: Optional[torch.Tensor]) -> _abi.KdaTensor:
-    """Descriptor of a tensor view (sizes and strides in elements)."""
-    d = _abi.KdaTensor()
+    """Descriptor of a tensor view (sizes and strides in elements).  Built
+    in one constructor call: this runs for a dozen tensors per launch."""
     if t is None:
-        return d
-    if t.dim() > 4:
+        return _abi.KdaTensor()
+    nd = t.dim()
+    if nd > 4:
         raise ValueError("tensors of at most 4 dimensions")
-    d.data = t.data_ptr()
-    d.dtype = _DT.get(t.dtype, -1)
-    d.ndim = t.dim()
-    for i in range(t.dim()):
-        d.shape[i] = t.shape[i]
-        d.stride[i] = t.stride(i)
-    return d
+    pad = _PAD[nd]
+    return _abi.KdaTensor(t.data_ptr(), _DT.get(t.dtype, -1), nd,
+                          _DIMS4(*t.shape, *pad), _DIMS4(*t.stride(), *pad))
 
 
 def _ptr(t: Optional[torch.Tensor]):
