@@ -13,6 +13,7 @@ Functions mirror the pages' host API:
 from __future__ import annotations
 
 import ctypes
+import struct
 from typing import Optional, Sequence
 
 import torch
@@ -61,6 +62,42 @@ def describe(t: Optional[torch.Tensor]) -> _abi.KdaTensor:
                           _DIMS4(*t.shape, *pad), _DIMS4(*t.stride(), *pad))
 
 
+def _pack_format(cls) -> str:
+    """struct-module format of a ctypes type in its C layout (explicit
+    padding bytes, little-endian, standard sizes)."""
+    if issubclass(cls, ctypes.Structure):
+        fmt, pos = "", 0
+        for name, ftype in cls._fields_:
+            off = getattr(cls, name).offset
+            fmt += f"{off - pos}x" if off > pos else ""
+            fmt += _pack_format(ftype)
+            pos = off + ctypes.sizeof(ftype)
+        end = ctypes.sizeof(cls)
+        return fmt + (f"{end - pos}x" if end > pos else "")
+    if issubclass(cls, ctypes.Array):
+        return _pack_format(cls._type_) * cls._length_
+    if cls is ctypes.c_void_p or issubclass(cls, ctypes._Pointer):
+        return "Q"
+    if cls is ctypes.c_float:
+        return "f"
+    return {4: "i", 8: "q"}[ctypes.sizeof(cls)]
+
+
+# KdaTensor as 11 values: data, dtype, ndim, 4 sizes, 4 strides
+_NO_TENSOR = (0, 0, 0) + (0,) * 8
+
+
+def _tensor_values(t: Optional[torch.Tensor]) -> tuple:
+    if t is None:
+        return _NO_TENSOR
+    nd = t.dim()
+    if nd > 4:
+        raise ValueError("tensors of at most 4 dimensions")
+    pad = _PAD[nd]
+    return (t.data_ptr(), _DT.get(t.dtype, -1), nd, *t.shape, *pad,
+            *t.stride(), *pad)
+
+
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
@@ -79,6 +116,9 @@ def _stream(stream) -> int:
     return int(stream)
 
 
+_VERIFY_PACK = struct.Struct("<" + _pack_format(_abi.KdaVerifyArgs))
+
+
 def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
                 lower_bound, state, correction, key_gate, out, conv_state,
                 conv_weight, query_start_loc, state_indices,
@@ -87,36 +127,26 @@ def verify_args(*, mixed_qkv, raw_gate, raw_beta, A_log, dt_bias,
                 max_workgroups=0, items_per_ticket=0,
                 schedule=0, pending_lens=None,
                 v_tiles=0) -> _abi.KdaVerifyArgs:
-    a = _abi.KdaVerifyArgs()
-    a.mixed_qkv = describe(mixed_qkv)
-    a.raw_gate = describe(raw_gate)
-    a.raw_beta = describe(raw_beta)
-    a.A_log = describe(A_log)
-    a.dt_bias = describe(dt_bias)
-    a.state = describe(state)
-    a.correction = describe(correction)
-    a.key_gate = describe(key_gate)
-    a.out = describe(out)
-    a.conv_state = describe(conv_state)
-    a.conv_weight = describe(conv_weight)
-    a.query_start_loc = _ptr(query_start_loc)
-    a.state_indices = _ptr(state_indices)
-    a.num_accepted_tokens = _ptr(num_accepted_tokens)
-    a.record_rows = _ptr(record_rows)
-    a.work_counter = _ptr(work_counter)
-    a.batch = state_indices.shape[0]
-    a.spec_query_len = spec_query_len
-    a.null_block_id = null_block_id
-    a.conv_dim_first = 1 if conv_dim_first else 0
-    a.use_lower_bound = 0 if lower_bound is None else 1
-    a.lower_bound = 0.0 if lower_bound is None else float(lower_bound)
-    a.max_workgroups = max_workgroups
-    a.items_per_ticket = items_per_ticket
-    a.schedule = schedule
-    a.pending_lens = _ptr(pending_lens)
-    a.work_counter_len = 0 if work_counter is None else work_counter.numel()
-    a.v_tiles = v_tiles
-    return a
+    """kda_verify_args for these tensors, packed in one struct-module call
+    (field order and layout of `_abi.KdaVerifyArgs`)."""
+    vals = (*_tensor_values(mixed_qkv), *_tensor_values(raw_gate),
+            *_tensor_values(raw_beta), *_tensor_values(A_log),
+            *_tensor_values(dt_bias), *_tensor_values(state),
+            *_tensor_values(correction), *_tensor_values(key_gate),
+            *_tensor_values(out), *_tensor_values(conv_state),
+            *_tensor_values(conv_weight),
+            _ptr(query_start_loc) or 0, _ptr(state_indices) or 0,
+            _ptr(num_accepted_tokens) or 0, _ptr(record_rows) or 0,
+            _ptr(work_counter) or 0,
+            state_indices.shape[0], spec_query_len, null_block_id,
+            1 if conv_dim_first else 0,
+            0 if lower_bound is None else 1,
+            0.0 if lower_bound is None else float(lower_bound),
+            max_workgroups, items_per_ticket, schedule,
+            _ptr(pending_lens) or 0,
+            0 if work_counter is None else work_counter.numel(),
+            v_tiles)
+    return _abi.KdaVerifyArgs.from_buffer_copy(_VERIFY_PACK.pack(*vals))
 
 
 def check_verify(**kwargs) -> int:
@@ -283,6 +313,7 @@ class CommitContext:
              col("key_gate", lambda t: t.stride(0))], dtype=torch.int64)
         self._host_tables = host.contiguous()
         self.tables = self._host_tables.to(dev)
+        self._fixed: Optional[bytes] = None   # constant argument fields
         self.A_log = torch.stack([L["A_log"].float() for L in layers]) \
             .contiguous().to(dev)
         self.dt_bias = torch.stack(
@@ -316,13 +347,11 @@ class CommitContext:
                  [c.stride(2) for c in convs]], dtype=torch.int64)
             self.conv_tables = self._host_conv_tables.to(dev)
 
-    def args(self, state_indices, commit_lens, final_state_indices=None,
-             record_rows=None, max_workgroups=0,
-             boundary_state_indices=None,
-             boundary_recovery_lens=None) -> _abi.KdaCommitArgs:
+    def _constant_args(self) -> bytes:
+        """The fields of kda_commit_args that do not change between steps
+        (sizes, address tables, strides, gate parameters), built once."""
         a = _abi.KdaCommitArgs()
         a.num_layers = self.num_layers
-        a.batch = state_indices.shape[0]
         a.num_heads = self.H
         a.head_dim = self.D
         a.spec_query_len = self.Q
@@ -341,19 +370,29 @@ class CommitContext:
         a.correction_strides[:] = list(self.correction_strides)
         a.key_gate_strides[:] = list(self.key_gate_strides)
         a.key_gate_dtype = self.key_gate_dtype
-        a.max_workgroups = max_workgroups
         a.A_log = self.A_log.data_ptr()
         a.A_log_strides[:] = list(self.A_log.stride())
         a.dt_bias = self.dt_bias.data_ptr()
         a.dt_bias_strides[:] = list(self.dt_bias.stride())
         a.use_lower_bound = self.use_lower_bound.data_ptr()
         a.lower_bound = self.lower_bound.data_ptr()
+        a.host_tables = self._host_tables.numpy().ctypes.data_as(
+            ctypes.POINTER(ctypes.c_int64))
+        return bytes(a)
+
+    def args(self, state_indices, commit_lens, final_state_indices=None,
+             record_rows=None, max_workgroups=0,
+             boundary_state_indices=None,
+             boundary_recovery_lens=None) -> _abi.KdaCommitArgs:
+        if self._fixed is None:
+            self._fixed = self._constant_args()
+        a = _abi.KdaCommitArgs.from_buffer_copy(self._fixed)
+        a.batch = state_indices.shape[0]
+        a.max_workgroups = max_workgroups
         a.state_indices = _ptr(state_indices)
         a.commit_lens = _ptr(commit_lens)
         a.final_state_indices = _ptr(final_state_indices)
         a.record_rows = _ptr(record_rows)
-        a.host_tables = self._host_tables.numpy().ctypes.data_as(
-            ctypes.POINTER(ctypes.c_int64))
         a.boundary_state_indices = _ptr(boundary_state_indices)
         a.boundary_recovery_lens = _ptr(boundary_recovery_lens)
         return a

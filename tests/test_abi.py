@@ -510,3 +510,69 @@ def test_vtile_schedule_checks():
     for k in ("conv_state", "conv_weight", "num_accepted_tokens"):
         kw[k] = None
     assert kda.check_verify_qkv(**kw) == 0, kda.load().kda_last_error()
+
+
+def _fieldwise_verify_args(kw):
+    """kda_verify_args built field by field through ctypes (the reference
+    for the packed marshalling)."""
+    a = _abi.KdaVerifyArgs()
+    for name in ("mixed_qkv", "raw_gate", "raw_beta", "A_log", "dt_bias",
+                 "state", "correction", "key_gate", "out", "conv_state",
+                 "conv_weight"):
+        t = kw.get(name)
+        d = _abi.KdaTensor()
+        if t is not None:
+            d.data = t.data_ptr()
+            d.dtype = {torch.float32: _abi.KDA_F32,
+                       torch.bfloat16: _abi.KDA_BF16}.get(t.dtype, -1)
+            d.ndim = t.dim()
+            for i in range(t.dim()):
+                d.shape[i] = t.shape[i]
+                d.stride[i] = t.stride(i)
+        setattr(a, name, d)
+    for name in ("query_start_loc", "state_indices", "num_accepted_tokens",
+                 "record_rows", "work_counter", "pending_lens"):
+        t = kw.get(name)
+        setattr(a, name, None if t is None else t.data_ptr())
+    a.batch = kw["state_indices"].shape[0]
+    a.spec_query_len = kw["spec_query_len"]
+    a.null_block_id = kw.get("null_block_id", 0)
+    a.conv_dim_first = 1 if kw["conv_dim_first"] else 0
+    lb = kw.get("lower_bound")
+    a.use_lower_bound = 0 if lb is None else 1
+    a.lower_bound = 0.0 if lb is None else float(lb)
+    a.max_workgroups = kw.get("max_workgroups", 0)
+    a.items_per_ticket = kw.get("items_per_ticket", 0)
+    a.schedule = kw.get("schedule", 0)
+    wc = kw.get("work_counter")
+    a.work_counter_len = 0 if wc is None else wc.numel()
+    a.v_tiles = kw.get("v_tiles", 0)
+    return a
+
+
+def test_packed_verify_args_match_fieldwise_ctypes():
+    """The one-call packed argument block is byte for byte the structure
+    ctypes builds field by field (layouts, dtypes, optional tensors,
+    scalars)."""
+    from linear_attention_speculative_amd import ops
+    cases = []
+    for dim_first in (True, False):
+        wl, kw = _kw(conv_dim_first=dim_first, act="f32", weight="f32")
+        cases.append(kw)
+    wl, kw = _kw(lower_bound=-5.0, kg_dtype="act", out_dtype="act")
+    kw.update(record_rows=torch.arange(wl.B, dtype=torch.int32),
+              pending_lens=torch.ones(wl.B, dtype=torch.int32),
+              null_block_id=3, max_workgroups=7, items_per_ticket=2,
+              schedule=2, v_tiles=4)
+    cases.append(kw)
+    kw2 = dict(kw, conv_state=None, conv_weight=None,
+               num_accepted_tokens=None, work_counter=None)
+    cases.append(kw2)
+    # a transposed (strided) output view
+    kw3 = dict(cases[0])
+    kw3["out"] = kw3["out"].t().contiguous().t()
+    cases.append(kw3)
+    for kw in cases:
+        packed = bytes(ops.verify_args(**kw))
+        ref = bytes(_fieldwise_verify_args(kw))
+        assert packed == ref
