@@ -168,6 +168,17 @@ __device__ __forceinline__ constexpr int idx_n(int t, int s) {
   return 2 * QMAX + QMAX * (QMAX - 1) / 2 + t * (t + 1) / 2 + s;
 }
 
+// The verify's output, correction and record stores: plain, or streamed
+// past the caches (non-temporal) at Q >= 8, where that measured 3% faster on
+// the 24-layer batch (at Q = 4 it measured 1% slower).
+template <int QMAX, class T>
+__device__ __forceinline__ void put_result(T* p, T v) {
+  if constexpr (QMAX >= 8)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
 // Wave-uniform description of one (request, head) work item.
 struct Item {
   int b, h, bos, q, slot, r, a;
@@ -492,9 +503,9 @@ __device__ __forceinline__ void item_front(
           sm.y[part][t][d] = yv;
           if (part == 1 && rec_ok && own_col(d)) {
             if (kg_bf16)
-              kg16[t * s_kp + d] = f32_to_bf16(yv);
+              put_result<QMAX>(&kg16[t * s_kp + d], f32_to_bf16(yv));
             else
-              kg32[t * s_kp + d] = yv;
+              put_result<QMAX>(&kg32[t * s_kp + d], yv);
           }
           s0 = s1;
           s1 = s2;
@@ -520,9 +531,9 @@ __device__ __forceinline__ void item_front(
       sm.dec[t][k] = __expf(kda_gate(g0 + hr.gb[jj], Ah, use_lb, p.lb));
       if (rec_ok && own_col(k)) {
         if (kg_bf16)
-          kg16[t * s_kp + D + k] = f32_to_bf16(g0);
+          put_result<QMAX>(&kg16[t * s_kp + D + k], f32_to_bf16(g0));
         else
-          kg32[t * s_kp + D + k] = g0;
+          put_result<QMAX>(&kg32[t * s_kp + D + k], g0);
       }
     }
   }
@@ -835,10 +846,11 @@ __device__ __forceinline__ void item_back(const VerifyParams& p,
 #pragma unroll
         for (int s = 0; s <= t; ++s) o = fmaf(sm.Nc[t][s], cc[s], o);
         if (p.flags & kOutBf16)
-          at(out16, uint32_t(t * s_out + v)) = f32_to_bf16(o);
+          put_result<QMAX>(&at(out16, uint32_t(t * s_out + v)),
+                           f32_to_bf16(o));
         else
-          at(out32, uint32_t(t * s_out + v)) = o;
-        if (rec_ok) at(corr, uint32_t(t * s_cp + v)) = cc[t];
+          put_result<QMAX>(&at(out32, uint32_t(t * s_out + v)), o);
+        if (rec_ok) put_result<QMAX>(&at(corr, uint32_t(t * s_cp + v)), cc[t]);
       }
     }
   }
