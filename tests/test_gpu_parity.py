@@ -174,15 +174,17 @@ def test_sweep_head_dim_and_window(D, Q, act):
 @pytest.mark.parametrize("out_dtype,kg_dtype", [("act", "f32"),
                                                 ("f32", "act"),
                                                 ("act", "act")])
-def test_activation_dtype_outputs_and_records(out_dtype, kg_dtype):
-    wl = make_workload("ragged", DEV, B=12, H=4, D=128, Q=4, N=20,
+@pytest.mark.parametrize("Q", [4, 8])
+def test_activation_dtype_outputs_and_records(out_dtype, kg_dtype, Q):
+    # (Q = 8 stores its results non-temporally, Q = 4 with plain stores)
+    wl = make_workload("ragged", DEV, B=12, H=4, D=128, Q=Q, N=20,
                        out_dtype=out_dtype, kg_dtype=kg_dtype)
     # A bf16 key record (the ops page's layout): the oracle's verify rounds
     # its fp64 key to bf16 and its commit folds those records; the bounds
     # widen by one bf16 step (see kg_extra_tol).
     sample, ref, errs = _verify_case(wl)
     cerr = _commit_case(wl, {0: (sample, ref)})
-    print("act records", out_dtype, kg_dtype, errs, cerr)
+    print("act records", out_dtype, kg_dtype, Q, errs, cerr)
 
 
 def test_bf16_out_is_rne_of_fp32_out():
