@@ -440,8 +440,9 @@ int plan_verify(const kda_verify_args* a, VerifyPlan* plan, bool conv,
     if (vt == 0) vt = default_vtiles(items);
   }
   // The default schedule never takes V-tiles: measured on MI355X they are
-  // not faster than whole items at any batch (one request: 8.2 us per
-  // verify either way; 64 requests: 41.0 us whole, 41.6 us with 2 tiles).
+  // not faster than whole items at any batch (one request: 6.9 us per
+  // verify whole, 7.0 / 7.1 / 9.0 us with 2 / 4 / 8 tiles; 64 ragged
+  // requests: 33.3 us whole, 34.7 / 43.8 / 68.6 us).
   // The verify of a small batch is bound by the latency of its phases,
   // which splitting the rows does not shorten.
   if (schedule == KDA_SCHEDULE_V_TILES && items * vt > 0x7fffffff)
