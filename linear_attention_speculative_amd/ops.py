@@ -45,21 +45,7 @@ def _raise(code: int):
     raise cls(code, msg)
 
 
-_DIMS4 = ctypes.c_int64 * 4
 _PAD = ((0, 0, 0, 0), (0, 0, 0), (0, 0), (0,), ())
-
-
-def describe(t: Optional[torch.Tensor]) -> _abi.KdaTensor:
-    """Descriptor of a tensor view (sizes and strides in elements).  Built
-    in one constructor call: this runs for a dozen tensors per launch."""
-    if t is None:
-        return _abi.KdaTensor()
-    nd = t.dim()
-    if nd > 4:
-        raise ValueError("tensors of at most 4 dimensions")
-    pad = _PAD[nd]
-    return _abi.KdaTensor(t.data_ptr(), _DT.get(t.dtype, -1), nd,
-                          _DIMS4(*t.shape, *pad), _DIMS4(*t.stride(), *pad))
 
 
 def _pack_format(cls) -> str:
@@ -85,6 +71,7 @@ def _pack_format(cls) -> str:
 
 # KdaTensor as 11 values: data, dtype, ndim, 4 sizes, 4 strides
 _NO_TENSOR = (0, 0, 0) + (0,) * 8
+_TENSOR_PACK = struct.Struct("<" + _pack_format(_abi.KdaTensor))
 
 
 def _tensor_values(t: Optional[torch.Tensor]) -> tuple:
@@ -96,6 +83,13 @@ def _tensor_values(t: Optional[torch.Tensor]) -> tuple:
     pad = _PAD[nd]
     return (t.data_ptr(), _DT.get(t.dtype, -1), nd, *t.shape, *pad,
             *t.stride(), *pad)
+
+
+def describe(t: Optional[torch.Tensor]) -> _abi.KdaTensor:
+    """Descriptor of a tensor view (sizes and strides in elements), for
+    callers that fill an argument structure themselves."""
+    return _abi.KdaTensor.from_buffer_copy(
+        _TENSOR_PACK.pack(*_tensor_values(t)))
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -512,24 +512,30 @@ def test_vtile_schedule_checks():
     assert kda.check_verify_qkv(**kw) == 0, kda.load().kda_last_error()
 
 
+_TENSOR_FIELDS = ("mixed_qkv", "raw_gate", "raw_beta", "A_log", "dt_bias",
+                  "state", "correction", "key_gate", "out", "conv_state",
+                  "conv_weight")
+
+
+def _fieldwise_tensor(t):
+    d = _abi.KdaTensor()
+    if t is not None:
+        d.data = t.data_ptr()
+        d.dtype = {torch.float32: _abi.KDA_F32,
+                   torch.bfloat16: _abi.KDA_BF16}.get(t.dtype, -1)
+        d.ndim = t.dim()
+        for i in range(t.dim()):
+            d.shape[i] = t.shape[i]
+            d.stride[i] = t.stride(i)
+    return d
+
+
 def _fieldwise_verify_args(kw):
     """kda_verify_args built field by field through ctypes (the reference
     for the packed marshalling)."""
     a = _abi.KdaVerifyArgs()
-    for name in ("mixed_qkv", "raw_gate", "raw_beta", "A_log", "dt_bias",
-                 "state", "correction", "key_gate", "out", "conv_state",
-                 "conv_weight"):
-        t = kw.get(name)
-        d = _abi.KdaTensor()
-        if t is not None:
-            d.data = t.data_ptr()
-            d.dtype = {torch.float32: _abi.KDA_F32,
-                       torch.bfloat16: _abi.KDA_BF16}.get(t.dtype, -1)
-            d.ndim = t.dim()
-            for i in range(t.dim()):
-                d.shape[i] = t.shape[i]
-                d.stride[i] = t.stride(i)
-        setattr(a, name, d)
+    for name in _TENSOR_FIELDS:
+        setattr(a, name, _fieldwise_tensor(kw.get(name)))
     for name in ("query_start_loc", "state_indices", "num_accepted_tokens",
                  "record_rows", "work_counter", "pending_lens"):
         t = kw.get(name)
@@ -576,3 +582,6 @@ def test_packed_verify_args_match_fieldwise_ctypes():
         packed = bytes(ops.verify_args(**kw))
         ref = bytes(_fieldwise_verify_args(kw))
         assert packed == ref
+        for name in _TENSOR_FIELDS:
+            t = kw.get(name)
+            assert bytes(ops.describe(t)) == bytes(_fieldwise_tensor(t))
