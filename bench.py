@@ -59,7 +59,8 @@ Other workloads (`--workload`), each one JSON line of the same form:
 The default run (headline) is the one the throughput figure is quoted on.
 `--cold-steps` times any workload that way (an evicting write and read
 before every timed step, the step timed from its first kernel's start to
-its last kernel's end).
+its last kernel's end by one pair of dispatch-recorded events; a pair per
+phase would add its own gap between the kernels).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold-steps]
   python bench.py --copy-calibration   # plain copy for HBM counter scaling
@@ -435,6 +436,16 @@ def main() -> int:
                 raise RuntimeError(f"phase {phases[i][0]} launched fewer "
                                    f"than {n} kernels")
 
+    def step_whole(pair):
+        # one (start, stop) pair around the whole step: the first launch's
+        # dispatch to the last launch's end, with no event between phases
+        total = sum(n for (_, _, n, _) in phases)
+        set_launch_events(pair[0], pair[1], total)
+        for (_, _, _, fn) in phases:
+            fn()
+        if set_launch_events(None, None, 0) != 0:
+            raise RuntimeError("a step launched fewer kernels than armed")
+
     def new_events():
         out = []
         for _ in range(P):
@@ -451,29 +462,37 @@ def main() -> int:
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     # The step time: K eager steps with nothing between the launches (cold
-    # steps: each after an untimed cache-evicting write, timed from its
-    # first kernel's start to its last kernel's end).
+    # steps: each after an untimed cache-evicting write and read, timed from
+    # its first kernel's start to its last kernel's end by one event pair
+    # that the library records from the kernels' own dispatch).
     events = [new_events() for _ in range(args.steps)]
+    whole = [new_events()[0] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         if evict is not None:
             evict_caches(evict, float(k))  # untimed: before the first kernel
-            step(events[k])
+            step_whole(whole[k])
         else:
             step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     if evict is not None:
-        ms_step = sum(e[0][0].elapsed_time(e[P - 1][1])
-                      for e in events) / args.steps
-    else:
-        # per-kernel durations: K more steps with every phase's launches
-        # timed from their own dispatch
-        for k in range(args.steps):
-            step(events[k])
-        torch.cuda.synchronize()
+        ms_step = sum(e[0].elapsed_time(e[1]) for e in whole) / args.steps
+    # per-kernel durations: K more steps (cold ones after the same eviction)
+    # with every phase's launches timed from their own dispatch
+    for k in range(args.steps):
+        if evict is not None:
+            evict_caches(evict, float(k) + 0.25)
+        step(events[k])
+    torch.cuda.synchronize()
+    if evict is not None:
+        ms_phased = sum(e[0][0].elapsed_time(e[P - 1][1])
+                        for e in events) / args.steps
+        print(f"# cold steps: {ms_step:.4f} ms/step with one event pair; "
+              f"{ms_phased:.4f} ms with an event pair per phase",
+              file=sys.stderr, flush=True)
     # per phase: microseconds per launch (a phase of n launches / n)
     per = [sorted(e[i][0].elapsed_time(e[i][1]) * 1e3 / phases[i][2]
                   for e in events) for i in range(P)]
