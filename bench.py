@@ -26,7 +26,9 @@ launches, and the
 median of single launches that each follow an untimed write and read of a
 1 GiB buffer (which evicts the caches and leaves no dirty lines for the
 timed kernel to write back), so that any help from the last-level cache
-between kernels shows up as a difference; `cpu_baseline`
+between kernels shows up as a difference; `cold_step` is the whole step
+after the same eviction (median of `--cold` steps, one event pair from the
+first kernel's dispatch to the last kernel's end); `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload;
 `step_hbm.frac_of_copy` relates the step's bandwidth to a plain 1 GiB
 device copy timed in the same run; `deferred_form` (headline only) times
@@ -557,6 +559,18 @@ def main() -> int:
         for i, (_, _, n, fn) in enumerate(phases):
             evict_caches(scratch, float(k) + 0.5 * i)
             cold[i].append(timed(fn, n))
+    # Whole cold steps (warm runs only; a --cold-steps run times its steps
+    # this way already): each after the eviction, one event pair from the
+    # first kernel's dispatch to the last kernel's end.
+    cold_step = []
+    if evict is None:
+        for k in range(args.cold):
+            evict_caches(scratch, float(k) + 0.75)
+            pair = new_events()[0]
+            step_whole(pair)
+            torch.cuda.synchronize()
+            cold_step.append(pair[0].elapsed_time(pair[1]))
+        cold_step.sort()
     del scratch
     for k in range(args.cold):
         for i, (_, _, n, fn) in enumerate(phases):
@@ -636,6 +650,13 @@ def main() -> int:
                for ph, m in zip(phases, mean_ms)},
             **{f"{ph[0]}_GB/s": ph[1] / ph[2] / (m * 1e-3) / 1e9
                for ph, m in zip(phases, mean_ms)}),
+        # the whole step after an untimed 1 GiB write and read (median of
+        # --cold steps)
+        "cold_step": None if not cold_step else {
+            "ms_per_step": quant(cold_step, 0.5),
+            "value": tokens / (quant(cold_step, 0.5) * 1e-3),
+            "frac": step_bytes / (quant(cold_step, 0.5) * 1e-3) / 1e9
+            / HBM_PEAK_GBS},
         "kernels": {
             ph[0]: {"median_us": quant(per[i], 0.5),
                     "p10_us": quant(per[i], 0.1),
