@@ -19,12 +19,12 @@
 // only per-head K-vector quantities.  That halves the per-element work of
 // the step-by-step form and keeps the state tile out of the critical path.
 //
-// The kernel is bound by instruction issue long before HBM unless every
-// per-item overhead is small, so: addresses are 32-bit offsets from
-// wave-uniform 64-bit bases; sigmoid/softplus use the hardware exp, log and
-// reciprocal; the K-dimension reductions go through an LDS tree instead of
-// one cross-lane reduction per scalar; the row dot products are reduced with
-// a transposing DPP reduction that leaves one finished value per lane.
+// With several items resident per compute unit the HBM traffic sets the
+// pace only if every per-item overhead is small, so: addresses are 32-bit
+// offsets from wave-uniform 64-bit bases; sigmoid/softplus use the hardware
+// exp, log and reciprocal; the K-dimension sums are reduced across lanes,
+// several scalars per step; the row dot products are reduced with a
+// transposing DPP reduction that leaves one finished value per lane.
 //
 // Phases of one item (LDS barriers between them):
 //   0  issue the small loads (conv history, new inputs, taps, gate, beta),
@@ -34,14 +34,19 @@
 //      update of the head's 3D channels (history at offset a-1 of the conv
 //      state, SiLU), roll the conv state in place, key record; gate decays
 //      and the raw-gate half of the key record; sigmoid(beta).
-//   1  per column k: partial sums of |k_t|^2, |q_t|^2 and of the pairwise
-//      terms <k_s, P_{s,t} k_t>, <k_s, P_{s,t} q_t>, summed over k in LDS.
-//   2  norms -> per-column vectors Gam_t k_hat_t, Gam_t q_hat_t (LDS) and the
-//      Q x Q coefficient matrices.
-//   3  dot products of every state row with the 2Q vectors; transposing
-//      reduction over the lanes that share a row; row results to LDS.
-//   4  one thread per row: triangular solve for c_t, outputs o_t; stores of
-//      out and of the correction record (coalesced along V).
+//   1  per column k: |k_t|^2, |q_t|^2 and the pairwise terms
+//      <k_s, P_{s,t} k_t>, <k_s, P_{s,t} q_t>, summed over k.  D >= 64: each
+//      wave sums over its 64 columns by a transposing lane reduction (one
+//      LDS word per scalar and wave) and the unnormalised column vectors
+//      Gam_t k_t, Gam_t q_t go to LDS; else an LDS tree.
+//   2  the Q x Q coefficient matrices and the 2Q norm factors (below
+//      D = 64 also the normalised column vectors).
+//   3  dot products of every state row with the 2Q column vectors;
+//      transposing reduction over the lanes that share a row; row results
+//      to LDS.
+//   4  one thread per row: row sums scaled by their norm factors, triangular
+//      solve for c_t, outputs o_t; stores of out and of the correction record
+//      (coalesced along V).
 #pragma once
 
 #include <utility>
