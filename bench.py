@@ -44,6 +44,9 @@ Other workloads (`--workload`), each one JSON line of the same form:
   align     the headline batch under prefix caching (16-token state
             blocks): verify of the running block, then the commit plan,
             conv compaction and align-mode commit in one fused launch;
+  unfused   the headline batch through the unfused verify
+            (kda_recoverssm_verify_qkv: q | k | v arrive convolved, no conv
+            state) and the commit;
   fused     the headline batch in the deferred form: each step is one
             launch that folds the previous step's accepted positions into
             the checkpoints and then verifies (the same verify and commit
@@ -115,7 +118,7 @@ def kernel_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, pending=None, boundary=None) -> dict:
+def algorithmic_bytes(wl, pending=None, boundary=None, conv=True) -> dict:
     """Bytes the method must move per launch (each state tile read once by
     the verify, read and written once by the commit; every activation,
     record and conv byte once), from the workload's seeded metadata.
@@ -123,7 +126,8 @@ def algorithmic_bytes(wl, pending=None, boundary=None) -> dict:
     records and writes the state tile back.  `boundary` (per request, the
     boundary length or 0): align mode also writes the boundary state, and
     the compaction moves three conv entries per channel to each of the
-    final and boundary slots."""
+    final and boundary slots.  `conv` False: the unfused verify (the input
+    row is already convolved: no taps, history or roll)."""
     import numpy as np
     H, D, Q, W = wl.H, wl.D, wl.Q, wl.W
     e_act = 2 if wl.act == "bf16" else 4
@@ -134,7 +138,8 @@ def algorithmic_bytes(wl, pending=None, boundary=None) -> dict:
     qsl = wl.query_start_loc.cpu().numpy().astype(np.int64)
     slots = wl.state_indices.cpu().numpy()
     lens = wl.commit_lens.cpu().numpy()
-    per_launch = C * W * e_w + 4 * H + 4 * H * D + 4 * (3 * wl.B + 1)
+    per_launch = (C * W * e_w if conv else 0) + 4 * H + 4 * H * D \
+        + 4 * (3 * wl.B + 1)
     verify = per_launch
     commit = 4 * H + 4 * H * D + 8 * wl.B   # gate params, slots + lens
     flush = 0
@@ -149,8 +154,9 @@ def algorithmic_bytes(wl, pending=None, boundary=None) -> dict:
             verify += q * H * D * e_out
             continue
         verify += 4 * H * D * D                          # state tile read
-        verify += (W - 1) * C * e_act                    # conv history
-        verify += (W - 2 + q) * C * e_act                # conv roll write
+        if conv:
+            verify += (W - 1) * C * e_act                # conv history
+            verify += (W - 2 + q) * C * e_act            # conv roll write
         verify += q * (C * e_act + H * D * e_act + H * e_act   # x, gate, beta
                        + H * D * e_out                   # out
                        + 4 * H * D + 2 * H * D * e_kg)   # records
@@ -232,6 +238,18 @@ def build_phases(name, wl, drive, torch, schedule=0, v_tiles=0):
                   commit)], nb["tokens"],
                 f"layers=1 align bs={bs}, {int((boundary > 0).sum())} "
                 "boundaries per step, fused commit step")
+    if name == "unfused":
+        nb = algorithmic_bytes(wl, conv=False)
+
+        def verify_qkv():
+            drive.verify_qkv(wl, 0, counter)
+
+        def commit_u():
+            ctx.commit(wl.state_indices, wl.commit_lens,
+                       record_rows=wl.record_rows)
+        return ([("kda_verify_grid_kernel", nb["verify"], 1, verify_qkv),
+                 ("kda_commit_grid_kernel", nb["commit"], 1, commit_u)],
+                nb["tokens"], "layers=1 unfused verify (convolved q|k|v)")
     nb = algorithmic_bytes(wl)
     vname = verify_kernel(wl, schedule, v_tiles)
 
@@ -410,7 +428,7 @@ def main() -> int:
     from workloads import make_workload
     from workloads import drive
 
-    cfg_name = "headline" if args.workload in ("align", "fused") \
+    cfg_name = "headline" if args.workload in ("align", "fused", "unfused") \
         else args.workload
     wl = make_workload(cfg_name, "cuda", out_dtype="act")
     phases, tokens, note = build_phases(args.workload, wl, drive, torch,
