@@ -44,6 +44,8 @@ Other workloads (`--workload`), each one JSON line of the same form:
   align     the headline batch under prefix caching (16-token state
             blocks): verify of the running block, then the commit plan,
             conv compaction and align-mode commit in one fused launch;
+  align3    the align workload with the commit step as three launches
+            (plan, conv compaction, commit);
   unfused   the headline batch through the unfused verify
             (kda_recoverssm_verify_qkv: q | k | v arrive convolved, no conv
             state) and the commit;
@@ -104,6 +106,8 @@ KERNEL_SOURCES = {
     "kda_verify_vtile_kernel": "kda_verify_kernels.hpp",
     "kda_verify_kernel": "kda_verify_kernels.hpp",
     "kda_commit_grid_kernel": "kda_commit.hip",
+    "kda_commit_plan_kernel": "kda_plan.hip",
+    "kda_compact_conv_kernel": "kda_plan.hip",
 }
 
 
@@ -208,8 +212,8 @@ def build_phases(name, wl, drive, torch, schedule=0, v_tiles=0):
                   L, fused)], nb["tokens"] * L,
                 f"layers={L} fused flush+verify, pending "
                 f"{int(wl.commit_lens.min())}..{int(wl.commit_lens.max())}")
-    ctx = drive.commit_context(wl, conv=name == "align")
-    if name == "align":
+    ctx = drive.commit_context(wl, conv=name in ("align", "align3"))
+    if name in ("align", "align3"):
         from workloads.gen import running_block_tables
         bs = ALIGN_BLOCK_SIZE
         table, computed = running_block_tables(
@@ -226,6 +230,38 @@ def build_phases(name, wl, drive, torch, schedule=0, v_tiles=0):
 
         def verify():
             conv_update_verify(**kw)
+
+        if name == "align3":
+            # the same commit step as three launches: plan, compaction,
+            # commit (the plan's four arrays carry between them)
+            plan_out = tuple(torch.empty(wl.B, dtype=torch.int32,
+                                         device="cuda") for _ in range(4))
+            lens_o, final_o, bnd_o, blens_o = plan_out
+
+            def plan():
+                ctx.plan(wl.commit_lens, wl.state_indices,
+                         wl.query_start_loc, block_table=table_t,
+                         num_computed_tokens=computed_t,
+                         mamba_block_size=bs, out=plan_out)
+
+            def compact():
+                ctx.compact(wl.state_indices, lens_o, final_o, bnd_o,
+                            blens_o)
+
+            def commit3():
+                ctx.commit(wl.state_indices, lens_o, final_o,
+                           boundary_state_indices=bnd_o,
+                           boundary_recovery_lens=blens_o)
+            # plan: metadata in (lens, slots, computed counts, one table
+            # entry, query starts), four int32 arrays out
+            plan_bytes = 4 * (wl.B + 1) + 4 * 4 * wl.B + 4 * 4 * wl.B
+            return ([("kda_verify_grid_kernel", nb["verify"], 1, verify),
+                     ("kda_commit_plan_kernel", plan_bytes, 1, plan),
+                     ("kda_compact_conv_kernel", nb["compact"], 1, compact),
+                     ("kda_commit_grid_kernel", nb["commit"], 1, commit3)],
+                    nb["tokens"],
+                    f"layers=1 align bs={bs}, {int((boundary > 0).sum())} "
+                    "boundaries per step, commit step as three launches")
 
         def commit():
             ctx.commit_step(wl.commit_lens, wl.state_indices,
@@ -428,7 +464,8 @@ def main() -> int:
     from workloads import make_workload
     from workloads import drive
 
-    cfg_name = "headline" if args.workload in ("align", "fused", "unfused") \
+    cfg_name = "headline" if args.workload in ("align", "align3", "fused",
+                                               "unfused") \
         else args.workload
     wl = make_workload(cfg_name, "cuda", out_dtype="act")
     phases, tokens, note = build_phases(args.workload, wl, drive, torch,
