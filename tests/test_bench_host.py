@@ -21,8 +21,9 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert "one GPU" in r.stderr or "single MI355X" in r.stderr
 
 
-def _count(wl, pending=None, boundary=None):
-    """Bytes of every tensor a launch must touch, request by request."""
+def _count(wl, pending=None, boundary=None, conv=True):
+    """Bytes of every tensor a launch must touch, request by request
+    (conv False: the unfused verify, which has no taps, history or roll)."""
     H, D, Q, W, B = wl.H, wl.D, wl.Q, wl.W, wl.B
     e = {"f32": 4, "bf16": 2}
     ea, ew, eo, ek = (e[wl.act], e[wl.weight], e[wl.out_dtype],
@@ -31,7 +32,7 @@ def _count(wl, pending=None, boundary=None):
     qsl = wl.query_start_loc.numpy()
     slots = wl.state_indices.numpy()
     lens = wl.commit_lens.numpy()
-    v = C * W * ew + 4 * H + 4 * H * D + 4 * (3 * B + 1)
+    v = (C * W * ew if conv else 0) + 4 * H + 4 * H * D + 4 * (3 * B + 1)
     c = 4 * H + 4 * H * D + 8 * B
     fl = cp = 0
     for b in range(B):
@@ -42,7 +43,8 @@ def _count(wl, pending=None, boundary=None):
             v += q * H * D * eo                    # zero rows only
             continue
         v += H * D * D * 4                         # checkpoint read
-        v += (W - 1) * C * ea + (W - 2 + q) * C * ea   # history, roll
+        if conv:
+            v += (W - 1) * C * ea + (W - 2 + q) * C * ea   # history, roll
         v += q * C * ea + q * H * D * ea + q * H * ea  # q|k|v, gate, beta
         v += q * H * D * eo                        # outputs
         v += q * (H * D * 4 + 2 * H * D * ek)      # records
@@ -75,6 +77,10 @@ def test_algorithmic_bytes_match_a_per_tensor_count():
                 got["compact"]) == (v, c, fl, cp), name
         qsl = wl.query_start_loc.numpy()
         assert got["tokens"] == int(np.minimum(np.diff(qsl), wl.Q).sum())
+        # the unfused verify: the same count without the conv terms
+        got = bench.algorithmic_bytes(wl, conv=False)
+        v, c, _, _ = _count(wl, conv=False)
+        assert (got["verify"], got["commit"]) == (v, c), name
 
 
 def test_running_block_tables():
